@@ -1,0 +1,29 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP path through the C ABI")
+    config.addinivalue_line("markers", "slow: large CPU work (full-size oracle or generator runs)")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests cannot run without a device; say so instead of failing deep inside HIP.
+    try:
+        import torch
+
+        have_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        have_gpu = False
+    if have_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU visible in this process")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)
