@@ -35,9 +35,12 @@ no weights or datasets are used.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
+from threadpoolctl import threadpool_limits
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "make_custom", "draw_normal", "round_to"]
 
@@ -162,9 +165,16 @@ def make_inputs(w: Workload | str, seed: int | None = None) -> dict:
 
         targets = rng.integers(0, w.Lk, size=(w.B, w.H, w.Lq))
         k64 = k.to(torch.float64).numpy()
-        for b in range(w.B):
-            for h in range(w.H):
-                q64[b, h] = _boost_head(q64[b, h], k64[b, h], targets[b, h], w.scale, w.boost)
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+        def one(bh):
+            b, h = bh
+            q64[b, h] = _boost_head(q64[b, h], k64[b, h], targets[b, h], w.scale, w.boost)
+
+        # heads are independent; single-threaded BLAS per head keeps the bits
+        # independent of the worker count
+        with threadpool_limits(1), ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+            list(ex.map(one, heads))
     q = round_to(q64, w.dtype)
     return dict(q=q, k=k, v=v, scale=w.scale, causal=w.causal, dtype=w.dtype, workload=w, targets=targets)
 

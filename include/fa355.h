@@ -1,0 +1,109 @@
+/*
+ * fa355.h — C ABI of libfa355: the fused, tiled attention forward pass on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, then the section on that page):
+ *   [DF] "FlashAttention数据流优化：MI50显存与带宽瓶颈实战"  (kwkr.cn/news/544806)
+ *   [AI] "AIInfra笔记01"                                   (kwkr.cn/news/547341)
+ *   [OP] "FlashAttention优化原理与工程实践"                (lbrq.cn/news/50349)
+ *
+ * The operation.  For every batch index b, head h and query row i:
+ *
+ *     s_ij    = scale * sum_d q[b,h,i,d] * k[b,h,j,d]            j visible to i
+ *     o[b,h,i,:] = sum_j exp(s_ij) * v[b,h,j,:] / sum_j exp(s_ij)
+ *     lse[b,h,i] = ln sum_j exp(s_ij)
+ *
+ * that is, scaled dot-product attention with a row softmax ([OP §2.1], the
+ * scores-times-scale, softmax, times-v form; [DF §2.1], the three stages QKᵀ,
+ * softmax, PV), computed without the score matrix ever reaching memory: the
+ * query rows are cut into tiles, key/value tiles stream past them, and each row
+ * keeps a running max and exp-sum that are folded into the output once all of
+ * its key tiles are seen ([DF §2.2], first and second layers; [OP §1], fusion
+ * and tiling).  The per-row log-sum-exp is the softmax statistic kept for a
+ * backward pass ([DF §2.2], third layer; [AI §3.2] sizes it as one float per
+ * row).  With causal != 0, key j is visible to row i iff j <= i ([DF §4.1],
+ * causal flag; diagonal included).
+ *
+ * Precision: q, k, v and o are fp16 or bf16; products are accumulated in fp32;
+ * the softmax runs in fp32 ([OP §4.1]: half-precision inputs, fp32 softmax
+ * accumulation).  The attention weights are rounded to the input type before
+ * they multiply v, and o is divided by the sum of those rounded weights; lse is
+ * taken from the fp32 sum.  o is rounded to nearest even.
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream (same type as hipStream_t; NULL = the null stream of the current device). */
+struct ihipStream_t;
+typedef struct ihipStream_t* fa_stream_t;
+
+typedef enum {
+  FA_DTYPE_F16 = 0,  /* IEEE binary16 */
+  FA_DTYPE_BF16 = 1  /* bfloat16 */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,         /* q, k, v, o or lse is NULL                                         */
+  FA_ERR_SHAPE = -2,        /* B, H, Lq or Lk < 1, or a size beyond the limits below              */
+  FA_ERR_HEAD_DIM = -3,     /* D is not 64 or 128                                                */
+  FA_ERR_DTYPE = -4,        /* dtype is not FA_DTYPE_F16 or FA_DTYPE_BF16                        */
+  FA_ERR_ALIGN = -5,        /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned        */
+  FA_ERR_SCALE = -6,        /* scale is NaN or infinite                                          */
+  FA_ERR_CAUSAL_SHAPE = -7, /* causal with Lq != Lk (the alignment of such a mask is undefined)  */
+  FA_ERR_DEVICE = -8,       /* the current device has no gfx950 code object for the kernel       */
+  FA_ERR_LAUNCH = -9        /* the kernel launch failed (HIP code in fa_last_hip_error())        */
+} fa_status;
+
+/*
+ * fa_fwd — enqueue one fused attention forward pass on `stream`.
+ *
+ * Arguments (all device pointers, allocated and owned by the caller):
+ *   q    [B, H, Lq, D]  dense row-major, element type `dtype`; read only.
+ *   k    [B, H, Lk, D]  dense row-major, `dtype`; read only.
+ *   v    [B, H, Lk, D]  dense row-major, `dtype`; read only.
+ *   o    [B, H, Lq, D]  dense row-major, `dtype`; written (every element).
+ *   lse  [B, H, Lq]     fp32; written (every element), natural log.
+ *   B, H, Lq, Lk        batch, heads, query rows, key rows (all >= 1).
+ *   D                   head dimension: 64 or 128.
+ *   scale               logit multiplier, any finite value (typically 1/sqrt(D));
+ *                       applied in fp32 to the fp32 dot products.
+ *   causal              0: every key is visible; non-zero: key j visible to row i iff
+ *                       j <= i, which requires Lq == Lk.
+ *   dtype               FA_DTYPE_F16 or FA_DTYPE_BF16 (q, k, v and o share it).
+ *   stream              HIP stream to enqueue on.
+ *
+ * Limits: Lq*D*2 + 256*D*2 and Lk*D*2 + 256*D*2 must stay below 2^32 bytes
+ * (one head's slab is addressed with 32-bit offsets, e.g. Lk < 16,777,000 at
+ * D = 128), and B*H*ceil(Lq/128) < 2^24 workgroups.
+ *
+ * Semantics: validation happens on the host before any HIP call; an invalid
+ * argument returns its FA_ERR_* code and enqueues nothing.  On success one
+ * kernel is enqueued and the call returns at once (asynchronous: o and lse are
+ * valid when the stream reaches that point).  The library allocates no memory,
+ * keeps no pointer after returning, never synchronises, never prints and never
+ * aborts.  o and lse must not overlap q, k or v (not checked).  The result is
+ * bitwise reproducible: the same inputs give the same bits on every call.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Lq, int Lk, int D, float scale, int causal, int dtype,
+           fa_stream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* The hipError_t behind the calling thread's last FA_ERR_LAUNCH or FA_ERR_DEVICE (0 if none). */
+int fa_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

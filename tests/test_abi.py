@@ -1,0 +1,150 @@
+"""The C ABI without a GPU: exported symbols, status strings, and every argument error.
+
+Invalid arguments are rejected on the host before any HIP call, so these run on
+a machine with no GPU.  No test here makes a call that would launch a kernel.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+import tiled_attention_06_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+# distinct, 16-byte aligned fake device addresses: never dereferenced on error paths
+P = [0x10000 * (i + 1) for i in range(5)]
+
+
+def declared_functions():
+    with open(HEADER, encoding="utf-8") as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", src, flags=re.M)
+
+
+def call(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Lq=64, Lk=64, D=128, scale=0.125, causal=0,
+         dtype=1):
+    return fa.lib.fa_fwd(q, k, v, o, lse, B, H, Lq, Lk, D, scale, causal, dtype, None)
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == ["fa_fwd", "fa_status_string", "fa_last_hip_error", "fa_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+        exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+        assert set(declared_functions()) <= exported
+
+
+def test_version_and_strings():
+    assert fa.fa_version() == 10000
+    for code in range(0, -10, -1):
+        s = fa.fa_status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in fa.fa_status_string(5)
+    assert fa.fa_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_null_pointers(which):
+    args = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4])
+    args[list(args)[which]] = None
+    assert call(**args) == -1
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("Lq", 0), ("Lk", 0), ("B", -3), ("Lk", -1),
+                                         ("Lq", 1 << 24), ("Lk", 16_777_000)])
+def test_shapes(field, value):
+    assert call(**{field: value}) == -2
+
+
+def test_workgroup_limit():
+    # B*H*ceil(Lq/128) must stay below 2^24 workgroups
+    assert call(B=1 << 12, H=1 << 12, Lq=128, Lk=128) == -2
+
+
+@pytest.mark.parametrize("D", [0, 32, 63, 96, 100, 127, 256])
+def test_head_dim(D):
+    assert call(D=D) == -3
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 3, 100])
+def test_dtype(dtype):
+    assert call(dtype=dtype) == -4
+
+
+@pytest.mark.parametrize("which,off", [("q", 8), ("k", 2), ("v", 4), ("o", 12), ("lse", 2), ("lse", 1)])
+def test_alignment(which, off):
+    args = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4])
+    args[which] += off
+    assert call(**args) == -5
+
+
+def test_lse_needs_only_4_byte_alignment_but_check_order_is_stable():
+    # lse at +4 is fine for alignment; make a later check fail so nothing launches
+    assert call(lse=P[4] + 4, D=96) == -3
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), float("-inf")])
+def test_scale(scale):
+    assert call(scale=scale) == -6
+
+
+def test_causal_requires_square():
+    assert call(causal=1, Lq=64, Lk=65) == -7
+    assert call(causal=7, Lq=3, Lk=2) == -7
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q)                      # CPU tensors
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q.float(), q.float(), q.float())
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q[0], q[0], q[0])             # not 4-D
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q[:, :, :2], q)            # k/v mismatch
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """The binding has no fallback: without libfa355.so the import raises ImportError."""
+    pkg = tmp_path / "tiled_attention_06_amd"
+    pkg.mkdir()
+    src = os.path.join(ROOT, "tiled_attention_06_amd")
+    for name in os.listdir(src):
+        if name.endswith(".py"):
+            shutil.copy(os.path.join(src, name), pkg / name)
+    res = subprocess.run([sys.executable, "-c", "import tiled_attention_06_amd"], cwd=tmp_path,
+                         capture_output=True, text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert res.returncode != 0
+    assert "ImportError" in res.stderr and "not built" in res.stderr
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """Nothing in the package imports the oracle or falls back to a CPU path."""
+    src = os.path.join(ROOT, "tiled_attention_06_amd")
+    for dirpath, _, files in os.walk(src):
+        for name in files:
+            if name.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                with open(os.path.join(dirpath, name), encoding="utf-8") as f:
+                    text = f.read()
+                assert "oracle" not in text.lower(), name
+                assert "scaled_dot_product_attention" not in text, name

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the same rounded inputs.
+
+Bar (per element): |O_gpu − O_ref| ≤ max(tol, ulp_dtype(O_ref)) with tol = 2e-3 (fp16) or
+1e-2 (bf16), and |LSE_gpu − LSE_ref| ≤ 1e-3.  The ulp term only matters where the
+output format itself cannot represent the exact value to within tol (|O| ≥ 4 in
+fp16, |O| ≥ 2 in bf16): there the rounding of a perfect result alone can exceed
+tol.  Every test also reports the plain max-abs error.
+
+Outputs are pre-filled with NaN so that an element the kernel fails to write fails
+the test.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import tiled_attention_06_amd as fa
+from oracle import attention_fp64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp16": 2e-3, "bf16": 1e-2}
+LSE_TOL = 1e-3
+MANT = {"fp16": (10, -14), "bf16": (7, -126)}
+DEV = "cuda:0"
+
+
+def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    bits, emin = MANT[dtype]
+    e = np.floor(np.log2(np.maximum(np.abs(x), 1e-300)))
+    return 2.0 ** (np.maximum(e, emin) - bits)
+
+
+def note(msg: str):
+    print(msg, flush=True)
+
+
+def run_gpu(inp, stream=None):
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fa.fa_fwd(q, k, v, o, lse, causal=inp["causal"], scale=inp["scale"], stream=stream)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def compare(o, lse, O_ref, L_ref, dtype, what=""):
+    o = o.double().cpu().numpy() if torch.is_tensor(o) else o
+    lse = lse.double().cpu().numpy() if torch.is_tensor(lse) else lse
+    assert np.isfinite(o).all(), f"{what}: non-finite O (unwritten or NaN)"
+    assert np.isfinite(lse).all(), f"{what}: non-finite LSE (unwritten or NaN)"
+    err = np.abs(o - O_ref)
+    bound = np.maximum(TOL[dtype], ulp(O_ref, dtype))
+    bad = err > bound
+    el = np.abs(lse - L_ref)
+    note(f"  {what}: max|dO|={err.max():.3e} max|dLSE|={el.max():.3e} max|O|={np.abs(O_ref).max():.2f}")
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: O error {err[i]:.4e} > bound {bound[i]:.4e} at {i} "
+                             f"(gpu {o[i]!r}, ref {O_ref[i]!r}); {int(bad.sum())} elements")
+    assert el.max() <= LSE_TOL, f"{what}: LSE error {el.max():.4e} at {np.unravel_index(el.argmax(), el.shape)}"
+    return float(err.max()), float(el.max())
+
+
+# ------------------------------------------------------------------------------------------
+# edge shapes (full comparison)
+# ------------------------------------------------------------------------------------------
+
+EDGE = [(1, 2, L, L, D, dt, c) for D in (64, 128) for dt in ("fp16", "bf16") for c in (False, True)
+        for L in (1, 2, 63, 64, 65, 127, 128, 129, 1000)]
+EDGE += [(1, 1, Lq, Lk, D, dt, False) for D in (64, 128) for dt in ("fp16", "bf16")
+         for (Lq, Lk) in ((1, 300), (200, 77), (129, 1000), (1000, 129), (64, 1))]
+EDGE += [(3, 5, 100, 100, 128, "bf16", True), (2, 3, 257, 257, 64, "fp16", True),
+         (1, 1, 4097, 4097, 128, "bf16", True), (1, 1, 4097, 4097, 64, "fp16", False)]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal", EDGE,
+                         ids=[f"B{b}H{h}_{lq}x{lk}_D{d}_{dt}_{'c' if c else 'nc'}" for b, h, lq, lk, d, dt, c in EDGE])
+def test_edge_shapes(B, H, Lq, Lk, D, dtype, causal):
+    seed = 10_000 + 97 * Lq + 13 * Lk + D + (1 if causal else 0) + (2 if dtype == "bf16" else 0)
+    inp = ai.make_custom(B, H, Lq, Lk, D, dtype, causal, seed=seed)
+    note(f"edge B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype} causal={causal} seed={seed}")
+    o, lse = run_gpu(inp)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], causal)
+    compare(o, lse, O_ref, L_ref, dtype, "edge")
+
+
+# ------------------------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the bench times
+# ------------------------------------------------------------------------------------------
+
+def _sample(w, seed=0):
+    r = np.random.default_rng(seed)
+    heads = {(0, 0), (w.B - 1, w.H - 1)}
+    while len(heads) < min(4, w.B * w.H):
+        heads.add((int(r.integers(w.B)), int(r.integers(w.H))))
+    rows = np.unique(np.concatenate([np.arange(min(32, w.Lq)), np.arange(max(0, w.Lq - 32), w.Lq),
+                                     r.integers(0, w.Lq, 64)]))
+    return sorted(heads), rows
+
+
+@pytest.mark.parametrize("name", list(ai.WORKLOADS))
+def test_workload(name):
+    w = ai.WORKLOADS[name]
+    note(f"workload {name}: generating inputs")
+    inp = ai.make_inputs(w)
+    note(f"workload {name}: GPU run {w.description}")
+    o, lse = run_gpu(inp)
+    o_c, lse_c = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert np.isfinite(o_c).all() and np.isfinite(lse_c).all(), "unwritten or non-finite output"
+    full = w.B * w.H * w.Lq * w.Lk <= 32 * 2048 * 2048
+    if full:
+        O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, w.causal)
+        compare(o_c, lse_c, O_ref, L_ref, w.dtype, f"{name} (all rows)")
+    else:
+        heads, rows = _sample(w)
+        O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, w.causal, rows=rows, heads=heads)
+        for b, h in heads:
+            compare(o_c[b, h][rows], lse_c[b, h][rows], O_ref[b, h], L_ref[b, h], w.dtype,
+                    f"{name} head ({b},{h}) {len(rows)} sampled rows")
+    # properties on every row: O is a convex combination of the visible V rows
+    v = inp["v"].double()
+    if w.causal:
+        lo = torch.cummin(v, dim=2).values.numpy()
+        hi = torch.cummax(v, dim=2).values.numpy()
+    else:
+        lo = v.min(dim=2, keepdim=True).values.numpy()
+        hi = v.max(dim=2, keepdim=True).values.numpy()
+    slack = ulp(np.maximum(np.abs(lo), np.abs(hi)), w.dtype)
+    assert (o_c >= lo - slack).all() and (o_c <= hi + slack).all(), "O outside the hull of visible V rows"
+    if w.causal:
+        # row 0 sees only key 0: its weight is exactly 1, so O equals v_0 bit for bit
+        assert torch.equal(o[:, :, 0].cpu(), inp["v"][:, :, 0])
+    if w.boost is not None:
+        # peaked softmax: O_i ≈ v_target (|O − v_t| ≤ 2·max|V|·(n−1)·e^−Δmin + rounding)
+        t = inp["targets"]
+        vt = np.take_along_axis(v.numpy(), t[..., None], axis=2)
+        dev_ = np.abs(o_c - vt).max()
+        note(f"  {name}: max|O - v_target| = {dev_:.3e}")
+        assert dev_ <= 2 * np.abs(v.numpy()).max() * (w.Lk - 1) * math.exp(-19.5) + 2 * TOL[w.dtype]
+
+
+# ------------------------------------------------------------------------------------------
+# GPU forms of the oracle's closed forms and invariants
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_zero_queries_give_prefix_means(dtype, causal):
+    inp = ai.make_custom(2, 2, 300, 300, 128, dtype, causal, seed=501)
+    inp["q"] = torch.zeros_like(inp["q"])
+    note(f"Q=0 {dtype} causal={causal}")
+    o, lse = run_gpu(inp)
+    v = inp["v"].double().numpy()
+    n = np.arange(1, 301) if causal else np.full(300, 300)
+    mean = np.cumsum(v, axis=2) / n[:, None] if causal else np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+    compare(o, lse, mean, np.broadcast_to(np.log(n), lse.shape), dtype, "Q=0")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_constant_values_are_exact(dtype):
+    inp = ai.make_custom(1, 3, 333, 333, 64, dtype, True, seed=502)
+    c = torch.tensor([0.75, -2.5, 1.0, 3.0] * 16).to(inp["v"].dtype)
+    inp["v"] = c.expand_as(inp["v"]).contiguous()
+    note(f"constant V {dtype}")
+    o, _ = run_gpu(inp)
+    assert torch.equal(o.cpu(), inp["v"]), "a constant V must come back exactly"
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_key_permutation_and_shift_invariance(dtype):
+    inp = ai.make_custom(1, 2, 200, 500, 128, dtype, False, seed=503)
+    note(f"invariance {dtype}")
+    o0, l0 = run_gpu(inp)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(500))
+    p = dict(inp, k=inp["k"][:, :, perm].contiguous(), v=inp["v"][:, :, perm].contiguous())
+    o1, l1 = run_gpu(p)
+    tol = TOL[dtype]
+    assert (o1.double() - o0.double()).abs().max().item() <= 2 * tol
+    assert (l1 - l0).abs().max().item() <= 2 * LSE_TOL
+    # a shift of every key by w moves LSE_i by scale·q_i·w and leaves O.  K is put on a
+    # grid of quarters in [-4, 4] first so that K and K + w are both exact in fp16/bf16.
+    kq = (inp["k"].double() * 4).round().clamp(-16, 16) / 4
+    base = dict(inp, k=kq.to(inp["k"].dtype))
+    w = torch.zeros(128, dtype=torch.float64)
+    w[::3] = 0.5
+    shifted = dict(inp, k=(kq + w).to(inp["k"].dtype))
+    assert torch.equal(shifted["k"].double(), kq + w)
+    o2, l2 = run_gpu(base)
+    o3, l3 = run_gpu(shifted)
+    shift = inp["scale"] * (inp["q"].double() @ w)
+    assert (o3.double() - o2.double()).abs().max().item() <= 2 * tol
+    assert (l3.double().cpu() - l2.double().cpu() - shift).abs().max().item() <= 2 * LSE_TOL
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1.7, 1e-3])
+def test_scale_values(scale):
+    inp = ai.make_custom(1, 2, 190, 190, 64, "bf16", True, seed=504)
+    inp["scale"] = scale
+    note(f"scale {scale}")
+    o, lse = run_gpu(inp)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], scale, True)
+    compare(o, lse, O_ref, L_ref, "bf16", f"scale={scale}")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_large_logits_running_max(dtype):
+    """Logits spread over hundreds of units: exercises the rescale of partial sums."""
+    inp = ai.make_custom(1, 2, 400, 400, 128, dtype, False, seed=505, sigma_q=6.0, sigma_k=4.0)
+    note(f"large logits {dtype}")
+    o, lse = run_gpu(inp)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], False)
+    compare(o, lse, O_ref, L_ref, dtype, "large logits")
+
+
+def test_bitwise_deterministic_and_stream():
+    inp = ai.make_custom(2, 4, 1000, 1000, 128, "bf16", True, seed=506)
+    note("determinism + non-default stream")
+    o0, l0 = run_gpu(inp)
+    for _ in range(2):
+        o1, l1 = run_gpu(inp)
+        assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = run_gpu(inp, stream=s)
+    assert torch.equal(o0, o2) and torch.equal(l0, l2)
+
+
+def test_outputs_written_into_given_buffers():
+    inp = ai.make_custom(1, 1, 77, 77, 64, "fp16", False, seed=507)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 1, 77), float("nan"), device=DEV)
+    o2, lse2 = fa.fa_fwd(q, k, v, o, lse)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == o.data_ptr() and lse2.data_ptr() == lse.data_ptr()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()

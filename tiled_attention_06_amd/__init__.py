@@ -1,0 +1,108 @@
+"""Python binding of libfa355, the gfx950 fused attention forward pass.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernel behind the C ABI declared in ``include/fa355.h``.  PyTorch supplies
+device memory and the current stream.  There is no fallback: if the compiled
+library is missing, importing this package raises ImportError.
+
+Names follow the C ABI: ``fa_fwd``, ``fa_status_string``, ``fa_last_hip_error``,
+``fa_version``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["fa_fwd", "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH",
+           "FA_DTYPE_F16", "FA_DTYPE_BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
+
+FA_DTYPE_F16 = 0
+FA_DTYPE_BF16 = 1
+_DTYPES = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libfa355.so is not built ({LIB_PATH} missing); build it with "
+            "`python tiled_attention_06_amd/build.py` or `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_last_hip_error.restype = i
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    return lib
+
+
+lib = _load()
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int):
+        self.code = code
+        super().__init__(f"{fa_status_string(code)} (status {code})")
+
+
+def fa_status_string(status: int) -> str:
+    return lib.fa_status_string(int(status)).decode()
+
+
+def fa_last_hip_error() -> int:
+    return int(lib.fa_last_hip_error())
+
+
+def fa_version() -> int:
+    return int(lib.fa_version())
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
+           lse: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
+           stream: torch.cuda.Stream | None = None):
+    """Enqueue ``fa_fwd`` on ``stream`` (default: torch's current stream of q's device).
+
+    q: [B, H, Lq, D]; k, v: [B, H, Lk, D]; contiguous fp16/bf16 tensors on one GPU.
+    o ([B, H, Lq, D], q's dtype) and lse ([B, H, Lq], float32) are allocated when
+    not given.  ``scale`` defaults to 1/sqrt(D).  Returns (o, lse).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, L, D]")
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    if tuple(k.shape) != (B, H, Lk, D) or tuple(v.shape) != (B, H, Lk, D):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    dev = q.device
+    if dev.type != "cuda" or k.device != dev or v.device != dev:
+        raise ValueError("q, k, v must be on the same GPU")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != q.dtype or o.device != dev or not o.is_contiguous():
+        raise ValueError("o must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+    elif tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or lse.device != dev or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Lq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    code = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      B, H, Lq, Lk, D, float(scale), 1 if causal else 0, _DTYPES[q.dtype], stream.cuda_stream)
+    if code != 0:
+        raise FaError(code)
+    return o, lse

@@ -1,0 +1,111 @@
+// libfa355: C ABI around the gfx950 attention forward kernel.
+//
+// Argument validation happens here, on the host, before any HIP call, so every
+// FA_ERR_* of a bad argument can be produced without a GPU.  A valid call
+// selects the kernel instance for (head dim, dtype, causal) and enqueues one
+// launch on the caller's stream.  No allocation, no synchronisation, no global
+// mutable state apart from the per-thread last HIP error.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "fa355.h"
+#include "fa_fwd_kernel.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+template <int D, int DT, bool CAUSAL>
+int launch(const fa355::FwdParams& p, hipStream_t stream) {
+  using G = fa355::Geo<D>;
+  hipLaunchKernelGGL((fa355::fa_fwd_kernel<D, DT, CAUSAL>), dim3(p.num_wg), dim3(G::NT), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = (int)e;
+  if (e == hipErrorInvalidDeviceFunction || e == hipErrorNoBinaryForGpu || e == hipErrorInvalidImage ||
+      e == hipErrorInvalidDevice)
+    return FA_ERR_DEVICE;
+  return FA_ERR_LAUNCH;
+}
+
+template <int D>
+int dispatch_dtype(const fa355::FwdParams& p, int dtype, bool causal, hipStream_t s) {
+  if (dtype == FA_DTYPE_BF16)
+    return causal ? launch<D, fa355::DT_BF16, true>(p, s) : launch<D, fa355::DT_BF16, false>(p, s);
+  return causal ? launch<D, fa355::DT_F16, true>(p, s) : launch<D, fa355::DT_F16, false>(p, s);
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk, int D,
+           float scale, int causal, int dtype, fa_stream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (causal && Lq != Lk) return FA_ERR_CAUSAL_SHAPE;
+
+  // One head's slab is addressed with 32-bit byte offsets, including up to 256
+  // rows of tile padding past its end.
+  const uint64_t row_bytes = (uint64_t)D * 2;
+  if (((uint64_t)Lq + 256) * row_bytes >= (1ull << 32) || ((uint64_t)Lk + 256) * row_bytes >= (1ull << 32))
+    return FA_ERR_SHAPE;
+  const int64_t n_qt = ((int64_t)Lq + 127) / 128;
+  const int64_t num_wg = (int64_t)B * H * n_qt;
+  if ((int64_t)B * H >= (1ll << 31) || num_wg >= (1ll << 24)) return FA_ERR_SHAPE;
+
+  fa355::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.Lq = Lq;
+  p.Lk = Lk;
+  p.n_qt = (int)n_qt;
+  p.num_wg = (int)num_wg;
+  p.xcd_remap = (num_wg % 8 == 0) ? 1 : 0;
+  // The softmax runs in base 2 with the scale folded into one positive factor;
+  // a negative scale negates Q (exact in fp16/bf16) and a zero scale zeroes it.
+  const double log2e = 1.4426950408889634074;
+  p.c = (float)((scale != 0.0f ? fabs((double)scale) : 1.0) * log2e);
+  p.q_and = scale == 0.0f ? 0u : 0xffffffffu;
+  p.q_xor = scale < 0.0f ? 0x80008000u : 0u;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return D == 128 ? dispatch_dtype<128>(p, dtype, causal != 0, s) : dispatch_dtype<64>(p, dtype, causal != 0, s);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "fa_fwd: a required pointer (q, k, v, o or lse) is NULL";
+    case FA_ERR_SHAPE: return "fa_fwd: B, H, Lq and Lk must be >= 1 and within the size limits";
+    case FA_ERR_HEAD_DIM: return "fa_fwd: head dimension D must be 64 or 128";
+    case FA_ERR_DTYPE: return "fa_fwd: dtype must be FA_DTYPE_F16 (0) or FA_DTYPE_BF16 (1)";
+    case FA_ERR_ALIGN: return "fa_fwd: q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_SCALE: return "fa_fwd: scale must be finite";
+    case FA_ERR_CAUSAL_SHAPE: return "fa_fwd: causal attention requires Lq == Lk";
+    case FA_ERR_DEVICE: return "fa_fwd: no gfx950 kernel for the current device";
+    case FA_ERR_LAUNCH: return "fa_fwd: kernel launch failed (see fa_last_hip_error)";
+    default: return "fa_fwd: unknown status code";
+  }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"
