@@ -1,0 +1,196 @@
+"""Throughput of the fused attention forward pass on one MI355X, as one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train7b_4k] [--no-cpu-baseline]
+
+One step = one ``fa_fwd`` call (the whole hot path: one kernel) over the
+workload's seeded synthetic Q, K, V, which are resident in HBM before timing
+starts.  The metric is attention-forward TFLOP/s with FLOP = 4·B·H·Lq·Lk·D,
+halved for causal, and its fraction of MI355X's dense bf16 MFMA peak.
+
+Besides the contract fields the line carries:
+  * ``roofline``: the kernel's algorithmic FLOP per launch divided by its mean
+    launch duration, measured with HIP events recorded on the launch stream
+    around every timed launch; ``traffic`` is the HBM bytes per launch from the
+    committed rocprofv3 counter summary, reported only while the kernel sources
+    still hash to what was profiled (else null);
+  * ``cpu_baseline``: the fp64 CPU oracle timed on this host over a bounded
+    sample of the same workload (whole heads, every row), as TFLOP/s-equivalent;
+  * ``parity``: a sampled comparison of this run's output with the oracle.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOP/s (bf16 causal, L=4096, D=128) and % of MFMA peak"
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_06_amd", "csrc", f) for f in ("fa_fwd_kernel.hpp", "fa355.hip")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_train7b_4k_traffic.md")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+    if workload != "train7b_4k" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE, encoding="utf-8") as f:
+        text = f.read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != kernel_source_hash():
+        return None
+    return float(b.group(1))
+
+
+def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
+    """The fp64 oracle, unmodified, over whole heads of the workload until ~budget_s of CPU work."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_head_fp64
+
+    w = inp["workload"]
+    q, k, v = (inp[n].double().numpy() for n in ("q", "k", "v"))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        attention_head_fp64(q[b, h], k[b, h], v[b, h], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops * done / len(heads)
+    threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of {w.name} (all {w.Lq} rows each), fp64 numpy, "
+                      f"{dt:.1f} s wall, BLAS threads={threads}"}
+
+
+def sampled_parity(inp, o, lse, n_rows: int = 128) -> dict:
+    import numpy as np
+
+    from oracle import attention_fp64
+
+    w = inp["workload"]
+    r = np.random.default_rng(1)
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(w.Lq - 16, w.Lq), r.integers(0, w.Lq, n_rows)]))
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, w.causal, rows=rows, heads=heads)
+    oc, lc = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    eo = max(float(np.abs(oc[b, h][rows] - O_ref[b, h]).max()) for b, h in heads)
+    el = max(float(np.abs(lc[b, h][rows] - L_ref[b, h]).max()) for b, h in heads)
+    tol = 2e-3 if w.dtype == "fp16" else 1e-2
+    return {"rows_checked": int(len(rows) * len(heads)), "max_abs_err_o": eo, "max_abs_err_lse": el,
+            "tol_o": tol, "tol_lse": 1e-3, "pass": bool(eo <= tol and el <= 1e-3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="train7b_4k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the attention forward pass runs on a single MI355X "
+              f"(requested --gpus {args.gpus}, WORLD_SIZE={world}). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import attn_inputs
+    import tiled_attention_06_amd as fa
+
+    w = attn_inputs.WORKLOADS[args.workload]
+    log(f"bench: {w.description}; generating inputs (seed {w.seed})")
+    inp = attn_inputs.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+
+    kernel_ms = [s.elapsed_time(e) for s, e in ev]
+    mean_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    value = w.flops * args.steps / wall / 1e12
+    achieved = w.flops / mean_kernel_s / 1e12
+    log(f"bench: {args.steps} steps in {wall * 1e3:.2f} ms; kernel mean {mean_kernel_s * 1e6:.1f} us "
+        f"(min {min(kernel_ms) * 1e3:.1f} us); {achieved:.1f} TFLOP/s = {100 * achieved / PEAK_BF16_TFLOPS:.2f}% of peak")
+
+    traffic = committed_traffic(w.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": w.causal,
+                   "scale": w.scale, "seed": w.seed, "flop_per_step": w.flops},
+        "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 5), "traffic": traffic,
+                     "kernel": f"fa_fwd_kernel<{w.D},{'bf16' if w.dtype == 'bf16' else 'f16'},"
+                               f"{'causal' if w.causal else 'full'}>",
+                     "mean_launch_us": round(mean_kernel_s * 1e6, 3)},
+    }
+    if not args.no_parity:
+        out["parity"] = sampled_parity(inp, o, lse)
+        log(f"bench: parity {out['parity']}")
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+        log(f"bench: cpu baseline {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
