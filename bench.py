@@ -1,11 +1,17 @@
 """Throughput of the fused attention forward pass on one MI355X, as one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train7b_4k] [--no-cpu-baseline]
+    python bench.py --traffic-probe          # for rocprofv3 --pmc runs (see below)
+    python bench.py --summarize-traffic DIR  # FETCH_SIZE/WRITE_SIZE CSVs -> profiles/*_traffic.md
+    python bench.py --summarize-trace DIR    # kernel-trace stats CSV -> profiles/*_kernel_trace.md
 
 One step = one ``fa_fwd`` call (the whole hot path: one kernel) over the
 workload's seeded synthetic Q, K, V, which are resident in HBM before timing
 starts.  The metric is attention-forward TFLOP/s with FLOP = 4·B·H·Lq·Lk·D,
 halved for causal, and its fraction of MI355X's dense bf16 MFMA peak.
+
+The shader clock of MI355X ramps over the first few hundred launches of this
+kernel, so the default warm-up is long (a few hundred milliseconds).
 
 Besides the contract fields the line carries:
   * ``roofline``: the kernel's algorithmic FLOP per launch divided by its mean
@@ -36,6 +42,8 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (bf16 causal, L=4096, D=128) and % of MFMA peak"
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_06_amd", "csrc", f) for f in ("fa_fwd_kernel.hpp", "fa355.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_train7b_4k_traffic.md")
+TRACE_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_train7b_4k_kernel_trace.md")
+COPY_BYTES = 1 << 30  # the plain device copy that calibrates the HBM byte counters
 
 
 def log(msg: str) -> None:
@@ -105,14 +113,128 @@ def sampled_parity(inp, o, lse, n_rows: int = 128) -> dict:
             "tol_o": tol, "tol_lse": 1e-3, "pass": bool(eo <= tol and el <= 1e-3)}
 
 
+def traffic_probe(w, steps: int) -> None:
+    """One plain device copy of COPY_BYTES (the counter calibration), then `steps` launches."""
+    import torch
+
+    import attn_inputs
+    import tiled_attention_06_amd as fa
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    del src, dst
+    inp = attn_inputs.make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    for _ in range(steps):
+        fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize(dev)
+    log(f"traffic probe: 1 copy of {COPY_BYTES} B, {steps} launches of fa_fwd on {w.name}")
+
+
+def _csv_rows(directory: str, name: str):
+    import csv
+    import glob
+
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", name), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_traffic(directory: str, w) -> str:
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of fa_fwd by the copy kernel's reading."""
+    rows = _csv_rows(directory, "*counter_collection.csv")
+    per = {}
+    for r in rows:
+        per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    copy = [(kn, c) for (kn, _), c in per.items() if "copy" in kn.lower() or "elementwise" in kn.lower()]
+    fa_ = [c for (kn, _), c in per.items() if "fa_fwd_kernel" in kn]
+    if not fa_:
+        raise SystemExit("no fa_fwd_kernel dispatches in the counter CSVs")
+    big = [c for _, c in copy if c.get("FETCH_SIZE", 0) * 1024 > COPY_BYTES / 2 or c.get("WRITE_SIZE", 0) * 1024 > COPY_BYTES / 2]
+    cf = [c["FETCH_SIZE"] for c in big if "FETCH_SIZE" in c]
+    cw = [c["WRITE_SIZE"] for c in big if "WRITE_SIZE" in c]
+    ff = [c["FETCH_SIZE"] for c in fa_ if "FETCH_SIZE" in c]
+    fw = [c["WRITE_SIZE"] for c in fa_ if "WRITE_SIZE" in c]
+    if not (cf and cw and ff and fw):
+        raise SystemExit("need FETCH_SIZE and WRITE_SIZE for both the copy and fa_fwd")
+    kf = COPY_BYTES / (sum(cf) / len(cf) * 1024)   # true bytes per counted byte, reads
+    kw = COPY_BYTES / (sum(cw) / len(cw) * 1024)   # and writes
+    fetch = sum(ff) / len(ff) * 1024 * kf
+    write = sum(fw) / len(fw) * 1024 * kw
+    alg = 2 * (2 * w.B * w.H * w.Lq * w.D + 2 * w.B * w.H * w.Lk * w.D) + 4 * w.B * w.H * w.Lq
+    lines = [
+        f"# HBM traffic of fa_fwd_kernel on {w.name} ({w.description})",
+        "",
+        "Counters from two `rocprofv3 --pmc` runs of `bench.py --traffic-probe` (one plain",
+        f"device copy of {COPY_BYTES} bytes, then {len(ff)} launches of fa_fwd); values are KiB",
+        "per dispatch.  Each counter is scaled by the copy kernel's true bytes / counted bytes.",
+        "",
+        "Commands (from the repository root on the GPU box):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic_fetch -o t -- python3 bench.py --traffic-probe",
+        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic_write -o t -- python3 bench.py --traffic-probe",
+        f"    python3 bench.py --summarize-traffic gpurun_out  (reads both directories)",
+        "",
+        f"copy kernel: FETCH_SIZE {sum(cf) / len(cf):.1f} KiB, WRITE_SIZE {sum(cw) / len(cw):.1f} KiB "
+        f"for {COPY_BYTES / 1024:.0f} KiB moved -> read factor {kf:.4f}, write factor {kw:.4f}",
+        f"fa_fwd: FETCH_SIZE {sum(ff) / len(ff):.1f} KiB, WRITE_SIZE {sum(fw) / len(fw):.1f} KiB per dispatch",
+        f"scaled: read {fetch:.4g} B, write {write:.4g} B per launch",
+        f"algorithmic bytes per launch (Q, K, V read once, O and LSE written once): {alg}",
+        f"traffic / algorithmic: {(fetch + write) / alg:.3f}",
+        "",
+        f"kernel_source_sha256: {kernel_source_hash()}",
+        f"hbm_bytes_per_launch: {fetch + write:.6g}",
+        "",
+    ]
+    return "\n".join(lines)
+
+
+def summarize_trace(directory: str, w, bench_line: str | None) -> str:
+    rows = _csv_rows(directory, "*kernel_stats.csv")
+    if not rows:
+        raise SystemExit("no kernel_stats.csv under " + directory)
+    keep = [r for r in rows if "fa_fwd_kernel" in r.get("Name", "")]
+    hdr = list(rows[0].keys())
+    lines = [
+        f"# rocprofv3 kernel trace: fa_fwd_kernel on {w.name} ({w.description})",
+        "",
+        "Command (from the repository root on the GPU box):",
+        "",
+        "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o t -- python3 bench.py --no-cpu-baseline --no-parity",
+        f"    python3 bench.py --summarize-trace gpurun_out/trace",
+        "",
+        "kernel_stats.csv rows for the kernel (durations in ns):",
+        "",
+        "| " + " | ".join(hdr) + " |",
+        "|" + "---|" * len(hdr),
+    ]
+    lines += ["| " + " | ".join(str(r[h]) for h in hdr) + " |" for r in keep]
+    if bench_line:
+        lines += ["", "bench.py JSON line of the same profiled run:", "", "    " + bench_line.strip()]
+    lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    return "\n".join(lines)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="train7b_4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true")
+    ap.add_argument("--summarize-traffic", metavar="DIR")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--bench-log", metavar="FILE", help="bench JSON line to quote in the trace summary")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -121,12 +243,33 @@ def main() -> int:
               f"(requested --gpus {args.gpus}, WORLD_SIZE={world}). Run with --gpus 1.", file=sys.stderr)
         return 2
 
-    import torch
-
     import attn_inputs
-    import tiled_attention_06_amd as fa
 
     w = attn_inputs.WORKLOADS[args.workload]
+    if args.summarize_traffic:
+        text = summarize_traffic(args.summarize_traffic, w)
+        with open(TRAFFIC_FILE, "w", encoding="utf-8") as f:
+            f.write(text)
+        print(text)
+        return 0
+    if args.summarize_trace:
+        line = None
+        if args.bench_log and os.path.exists(args.bench_log):
+            with open(args.bench_log, encoding="utf-8") as f:
+                line = next((x for x in f if x.startswith("{")), None)
+        text = summarize_trace(args.summarize_trace, w, line)
+        with open(TRACE_FILE, "w", encoding="utf-8") as f:
+            f.write(text)
+        print(text)
+        return 0
+
+    import torch
+
+    import tiled_attention_06_amd as fa
+
+    if args.traffic_probe:
+        traffic_probe(w, steps=3)
+        return 0
     log(f"bench: {w.description}; generating inputs (seed {w.seed})")
     inp = attn_inputs.make_inputs(w)
     dev = torch.device("cuda:0")

@@ -28,6 +28,7 @@ HIPCC_FLAGS = [
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    "-Wl,--no-undefined",  # a missing kernel stub must fail the build, not the first load
 ]
 
 

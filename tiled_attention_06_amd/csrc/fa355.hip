@@ -62,9 +62,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   const uint64_t row_bytes = (uint64_t)D * 2;
   if (((uint64_t)Lq + 256) * row_bytes >= (1ull << 32) || ((uint64_t)Lk + 256) * row_bytes >= (1ull << 32))
     return FA_ERR_SHAPE;
-  const int64_t n_qt = ((int64_t)Lq + 127) / 128;
+  const int BR = D == 128 ? fa355::Geo<128>::BR : fa355::Geo<64>::BR;
+  const int64_t n_qt = ((int64_t)Lq + BR - 1) / BR;
   const int64_t num_wg = (int64_t)B * H * n_qt;
-  if ((int64_t)B * H >= (1ll << 31) || num_wg >= (1ll << 24)) return FA_ERR_SHAPE;
+  if ((int64_t)B * H >= (1ll << 31) || num_wg >= (1ll << 22)) return FA_ERR_SHAPE;
 
   fa355::FwdParams p;
   p.q = q;
