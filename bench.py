@@ -121,10 +121,10 @@ def traffic_probe(w, steps: int) -> None:
     import tiled_attention_06_amd as fa
 
     dev = torch.device("cuda:0")
-    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)  # a fill: writes COPY_BYTES
     dst = torch.empty_like(src)
     torch.cuda.synchronize(dev)
-    dst.copy_(src)
+    torch.neg(src, out=dst)  # an elementwise kernel: reads and writes COPY_BYTES
     torch.cuda.synchronize(dev)
     del src, dst
     inp = attn_inputs.make_inputs(w)
@@ -154,13 +154,15 @@ def summarize_traffic(directory: str, w) -> str:
     per = {}
     for r in rows:
         per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
-    copy = [(kn, c) for (kn, _), c in per.items() if "copy" in kn.lower() or "elementwise" in kn.lower()]
     fa_ = [c for (kn, _), c in per.items() if "fa_fwd_kernel" in kn]
     if not fa_:
         raise SystemExit("no fa_fwd_kernel dispatches in the counter CSVs")
-    big = [c for _, c in copy if c.get("FETCH_SIZE", 0) * 1024 > COPY_BYTES / 2 or c.get("WRITE_SIZE", 0) * 1024 > COPY_BYTES / 2]
-    cf = [c["FETCH_SIZE"] for c in big if "FETCH_SIZE" in c]
-    cw = [c["WRITE_SIZE"] for c in big if "WRITE_SIZE" in c]
+    # Calibration dispatches: the fill and the elementwise kernel each write
+    # COPY_BYTES, and only the elementwise kernel also reads COPY_BYTES.
+    other = [c for (kn, _), c in per.items() if "fa_fwd_kernel" not in kn]
+    half_kib = COPY_BYTES / 2 / 1024
+    cf = [c["FETCH_SIZE"] for c in other if c.get("FETCH_SIZE", 0) > half_kib]
+    cw = [c["WRITE_SIZE"] for c in other if c.get("WRITE_SIZE", 0) > half_kib]
     ff = [c["FETCH_SIZE"] for c in fa_ if "FETCH_SIZE" in c]
     fw = [c["WRITE_SIZE"] for c in fa_ if "WRITE_SIZE" in c]
     if not (cf and cw and ff and fw):
@@ -173,9 +175,10 @@ def summarize_traffic(directory: str, w) -> str:
     lines = [
         f"# HBM traffic of fa_fwd_kernel on {w.name} ({w.description})",
         "",
-        "Counters from two `rocprofv3 --pmc` runs of `bench.py --traffic-probe` (one plain",
-        f"device copy of {COPY_BYTES} bytes, then {len(ff)} launches of fa_fwd); values are KiB",
-        "per dispatch.  Each counter is scaled by the copy kernel's true bytes / counted bytes.",
+        "Counters from two `rocprofv3 --pmc` runs of `bench.py --traffic-probe`: a fill of",
+        f"{COPY_BYTES} bytes, a plain elementwise copy of {COPY_BYTES} bytes to another buffer, then",
+        f"{len(ff)} launches of fa_fwd.  Values are KiB per dispatch.  Each counter is scaled by",
+        "the calibration kernels' true bytes / counted bytes.",
         "",
         "Commands (from the repository root on the GPU box):",
         "",
@@ -183,8 +186,9 @@ def summarize_traffic(directory: str, w) -> str:
         "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic_write -o t -- python3 bench.py --traffic-probe",
         f"    python3 bench.py --summarize-traffic gpurun_out  (reads both directories)",
         "",
-        f"copy kernel: FETCH_SIZE {sum(cf) / len(cf):.1f} KiB, WRITE_SIZE {sum(cw) / len(cw):.1f} KiB "
-        f"for {COPY_BYTES / 1024:.0f} KiB moved -> read factor {kf:.4f}, write factor {kw:.4f}",
+        f"calibration: FETCH_SIZE {sum(cf) / len(cf):.1f} KiB (mean of {len(cf)}), WRITE_SIZE "
+        f"{sum(cw) / len(cw):.1f} KiB (mean of {len(cw)}) for {COPY_BYTES / 1024:.0f} KiB moved -> "
+        f"read factor {kf:.4f}, write factor {kw:.4f}",
         f"fa_fwd: FETCH_SIZE {sum(ff) / len(ff):.1f} KiB, WRITE_SIZE {sum(fw) / len(fw):.1f} KiB per dispatch",
         f"scaled: read {fetch:.4g} B, write {write:.4g} B per launch",
         f"algorithmic bytes per launch (Q, K, V read once, O and LSE written once): {alg}",
