@@ -79,7 +79,7 @@ typedef enum {
  *
  * Limits: Lq*D*2 + 256*D*2 and Lk*D*2 + 256*D*2 must stay below 2^32 bytes
  * (one head's slab is addressed with 32-bit offsets, e.g. Lk < 16,777,000 at
- * D = 128), and B*H*ceil(Lq/128) < 2^22 workgroups.
+ * D = 128), and B*H*ceil(Lq/256) < 2^22 workgroups.
  *
  * Semantics: validation happens on the host before any HIP call; an invalid
  * argument returns its FA_ERR_* code and enqueues nothing.  On success one

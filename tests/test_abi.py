@@ -74,8 +74,9 @@ def test_shapes(field, value):
 
 
 def test_workgroup_limit():
-    # B*H*ceil(Lq/128) must stay below 2^24 workgroups
-    assert call(B=1 << 12, H=1 << 12, Lq=128, Lk=128) == -2
+    # B*H*ceil(Lq/256) must stay below 2^22 workgroups
+    assert call(B=1 << 11, H=1 << 11, Lq=256, Lk=256) == -2
+    assert call(B=1 << 10, H=1 << 11, Lq=257, Lk=257) == -2
 
 
 @pytest.mark.parametrize("D", [0, 32, 63, 96, 100, 127, 256])

@@ -5,20 +5,28 @@
 //   [AI] "AIInfra笔记01"                                   (kwkr.cn/news/547341)
 //   [OP] "FlashAttention优化原理与工程实践"                (lbrq.cn/news/50349)
 //
-// One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
-// 32 rows.  The method ([DF §2.2], first and second layers; [OP §2.1], a loop
-// over key blocks inside a loop over query blocks):
+// One workgroup = 8 waves (two per SIMD) = 256 query rows of one (batch, head);
+// each wave owns 32 rows.  One workgroup per CU.  The method ([DF §2.2], first
+// and second layers; [OP §2.1], a loop over key blocks inside a loop over query
+// blocks):
 //   * the Q tile is loaded once and stays in VGPRs as MFMA operands;
 //   * K and V tiles of BC keys are copied HBM -> LDS by the buffer unit itself
-//     (buffer_load ... lds, no VGPR staging), into two K and two V buffers: the
-//     copy of K tile j+2 and V tile j+1 runs while tile j is computed ([DF §2.3]
-//     prefetch of the next block);
+//     (buffer_load ... lds, no VGPR staging) into a ring of four stages: the
+//     copies of tile t+3 are issued while tile t is computed ([DF §2.3] prefetch
+//     of the next block, three tiles deep here).  Each iteration waits only for
+//     the tiles it needs next (an explicit vmcnt count) and joins the workgroup
+//     with a bare s_barrier, so later copies stay in flight across iterations;
+//   * in LDS, 1 KB copy block b of a tile holds rows b, b+NBLK, b+2·NBLK, ... and
+//     blocks are padded apart: every copy uses one per-lane offset, and the rows
+//     read together by an MFMA operand fall on distinct banks;
 //   * Sᵀ = K·Qᵀ runs on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation, so
 //     each lane holds 32 keys of ONE query row and the row max / row sums are
 //     in-lane plus one v_permlane32_swap with the other half-wave;
-//   * software pipelining inside each wave: the MFMAs of Sᵀ for tile j+1 are
-//     issued before the softmax of tile j, so the VALU work of one tile runs
-//     under the matrix work of the next;
+//   * full tiles are software-pipelined inside each wave: the MFMAs of Sᵀ for
+//     tile t+1 are issued in the same basic block as the softmax and PV of tile
+//     t, with the rescale decision for tile t taken from the max found one
+//     iteration earlier; tiles that cross the diagonal or the end of the keys
+//     run afterwards, unpipelined and masked;
 //   * online softmax in base 2 ([DF §2.2], second layer): t = S·(|scale|·log2 e),
 //     running max m and sums, exp on v_exp_f32.  The running max only moves when a
 //     tile's max exceeds it by more than TAU (then the partial output and sums
@@ -80,7 +88,7 @@ struct FwdParams {
   void* o;
   float* lse;
   int Lq, Lk;
-  int n_qt;         // query tiles per head: ceil(Lq / 128)
+  int n_qt;         // query tiles per head: ceil(Lq / BR)
   int num_wg;       // B * H * n_qt
   int xcd_remap;    // 1: group consecutive work items on one XCD
   float c;          // |scale| * log2(e), or log2(e) when scale == 0 (always > 0)
@@ -131,6 +139,24 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t of
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
 
+// One 16-byte-per-lane HBM -> LDS copy (buffer_load_dwordx4 ... lds): lane l's
+// 16 bytes land at LDS byte lds + 16·l.  Written as inline assembly so that the
+// compiler neither tracks nor waits for these LDS writes: the kernel orders them
+// itself with explicit vmcnt waits and barriers.  rsrc and lds must be uniform.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+#endif
+}
+
+// 32-bit LDS address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // max / sum of a value over lanes l and l^32 (every lane gets the result)
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -152,7 +178,7 @@ __device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
 // Tile geometry shared by the kernel and the host launcher.
 template <int D>
 struct Geo {
-  static constexpr int NW = 4;                 // waves per workgroup
+  static constexpr int NW = 8;                 // waves per workgroup (two per SIMD)
   static constexpr int NT = 64 * NW;           // threads per workgroup
   static constexpr int BR = 32 * NW;           // query rows per workgroup
   static constexpr int BC = 64;                // keys per K/V tile
@@ -160,27 +186,45 @@ struct Geo {
   static constexpr int NB = D / 32;            // 32-dim blocks of the output (Oᵀ MFMA row blocks)
   static constexpr int KS = D / 16;            // contraction steps of QKᵀ
   static constexpr int NCH = D / 8;            // 16-byte chunks per K/V row
-  // LDS row pitches in 16-byte chunks: the padding chunks spread the rows of one
-  // MFMA operand read over distinct banks.
-  static constexpr int KPC = NCH + 1;
-  static constexpr int VPC = NCH + 2;
-  static constexpr int KP = 16 * KPC, VP = 16 * VPC;  // bytes
-  static constexpr int KT = BC * KP, VT = BC * VP;    // bytes per K / V tile
-  static constexpr int KI = BC * KPC / 64, VI = BC * VPC / 64;  // 1 KB copy instructions per tile
-  static constexpr int LDS = 2 * KT + 2 * VT;
-  static_assert(BC * KPC % 64 == 0 && BC * VPC % 64 == 0, "tiles are whole 1 KB copy blocks");
-  static_assert(LDS <= 81920, "two workgroups per CU");
+  // LDS image of a K/V tile: NBLK blocks of 1 KB, one per copy instruction; block
+  // b holds the RPB rows b, b+NBLK, b+2·NBLK, ... back to back, and blocks are
+  // separated by a pad.  The pads put the rows read together by one MFMA operand
+  // read on distinct banks, and every copy needs the same per-lane source offset.
+  static constexpr int RPB = 512 / D;          // rows per block (4 at D=128, 8 at D=64)
+  static constexpr int NBLK = BC / RPB;        // blocks per tile
+  static constexpr int KBS = 1024 + 16;        // bytes per K block (rows 16 bytes apart in bank space)
+  static constexpr int VBS = 1024 + 64;        // bytes per V block (rows 64 bytes apart in bank space)
+  static constexpr int KT = NBLK * KBS, VT = NBLK * VBS;  // bytes per K / V tile
+  static constexpr int CPW = NBLK / NW;        // copy instructions per wave and tile
+  static constexpr int NS = 4;                 // K and V tiles resident in LDS (ring of stages)
+  static constexpr int LDS = NS * (KT + VT);
+  static_assert(NBLK % NW == 0 && 32 % NBLK == 0 && NBLK >= 8, "copy and read layout");
+  static_assert(LDS <= 163840, "one workgroup per CU");
 };
 
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(FwdParams p) {
   using G = Geo<D>;
   constexpr int BC = G::BC, KB = G::KB, NB = G::NB, KS = G::KS, NCH = G::NCH;
-  constexpr int KP = G::KP, VP = G::VP, KT = G::KT, VT = G::VT;
+  constexpr int NBLK = G::NBLK, KBS = G::KBS, VBS = G::VBS, KT = G::KT, VT = G::VT;
   constexpr float NEG_INF = -__builtin_inff();
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
-  unsigned char* const kbuf0 = smem;
-  unsigned char* const vbuf0 = smem + 2 * KT;
+  // One array per stage: the compiler can then tell that a tile copy in flight
+  // into one stage does not alias reads of another, and waits for it only where
+  // the code says so.
+  __shared__ __attribute__((aligned(16))) unsigned char ks0[KT], ks1[KT], ks2[KT], ks3[KT];
+  __shared__ __attribute__((aligned(16))) unsigned char vs0[VT], vs1[VT], vs2[VT], vs3[VT];
+  static_assert(G::NS == 4, "four stages");
+  auto kst = [&](auto Sc) -> unsigned char* {
+    constexpr int S = decltype(Sc)::value;
+    if constexpr (S == 0) return ks0; else if constexpr (S == 1) return ks1; else if constexpr (S == 2) return ks2;
+    else return ks3;
+  };
+  auto vst = [&](auto Sc) -> unsigned char* {
+    constexpr int S = decltype(Sc)::value;
+    if constexpr (S == 0) return vs0; else if constexpr (S == 1) return vs1; else if constexpr (S == 2) return vs2;
+    else return vs3;
+  };
+  using I0 = std::integral_constant<int, 0>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -202,36 +246,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const size_t qbase = (size_t)bh * (size_t)Lq * D * 2;
   const size_t kbase = (size_t)bh * (size_t)Lk * D * 2;
   const auto qrs = make_rsrc((const char*)p.q + qbase, (uint32_t)Lq * D * 2);
-  const auto krs = make_rsrc((const char*)p.k + kbase, (uint32_t)Lk * D * 2);
-  const auto vrs = make_rsrc((const char*)p.v + kbase, (uint32_t)Lk * D * 2);
   const auto ors = make_rsrc((char*)p.o + qbase, (uint32_t)Lq * D * 2);
 
-  // ---- HBM -> LDS copy of one tile.  LDS slot s (16 bytes) of the tile holds
-  // chunk s % PC of row s / PC; padding slots (chunk >= NCH) get a duplicate of
-  // chunk 0.  Keys >= Lk read 0 (outside the buffer range).
-  auto copy_tile = [&](__amdgpu_buffer_rsrc_t rs, unsigned char* dst, int key0, auto PCc, auto NIc) {
-    constexpr int PC = decltype(PCc)::value, NI = decltype(NIc)::value;
+  // ---- HBM -> LDS copy of one tile.  Copy j of wave w fills block b = w + NW·j:
+  // lane l brings the 16-byte chunk l % NCH of tile row b + NBLK·(l / NCH).  The
+  // buffer resource starts at the tile's first key and ends at the last key, so
+  // keys >= Lk read 0; the per-lane offset is the same for every tile.
+  const uint32_t lane_src = (uint32_t)((wave + NBLK * (lane / NCH)) * D * 2 + 16 * (lane % NCH));
+  const char* const kslab = (const char*)p.k + kbase;
+  const char* const vslab = (const char*)p.v + kbase;
+  auto copy_tile = [&](const char* slab, unsigned char* dst, int key0, auto BSc) {
+    constexpr int BS = decltype(BSc)::value;
+    const uint64_t base = (uint64_t)(uintptr_t)(slab + (size_t)key0 * D * 2);
+    const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xffffu)),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(Lk - key0) * D * 2)),
+                      (uint32_t)kBufferFlags};
+    const uint32_t l0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_addr(dst) + BS * wave));
 #pragma unroll
-    for (int bi0 = 0; bi0 < NI; bi0 += G::NW) {
-      const int bi = bi0 + wave;
-      if (bi < NI) {
-        const int s = 64 * bi + lane;
-        const int r = s / PC;
-        int ch = s - r * PC;
-        ch = ch < NCH ? ch : 0;
-        const uint32_t off = (uint32_t)((key0 + r) * D + 8 * ch) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + 1024 * bi), 16, off, 0, 0, 0);
-      }
-    }
+    for (int j = 0; j < G::CPW; ++j) dma16(rs, l0 + BS * G::NW * j, lane_src + G::NW * j * D * 2);
   };
-  auto copy_k = [&](int tile, int buf) {
-    copy_tile(krs, kbuf0 + buf * KT, tile * BC, std::integral_constant<int, G::KPC>{},
-              std::integral_constant<int, G::KI>{});
-  };
-  auto copy_v = [&](int tile, int buf) {
-    copy_tile(vrs, vbuf0 + buf * VT, tile * BC, std::integral_constant<int, G::VPC>{},
-              std::integral_constant<int, G::VI>{});
-  };
+  auto copy_k = [&](int tile, auto Sc) { copy_tile(kslab, kst(Sc), tile * BC, std::integral_constant<int, KBS>{}); };
+  auto copy_v = [&](int tile, auto Sc) { copy_tile(vslab, vst(Sc), tile * BC, std::integral_constant<int, VBS>{}); };
 
   // ---- key range of this workgroup
   int n_kv = (Lk + BC - 1) / BC;
@@ -240,10 +276,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     n_kv = min(n_kv, last_row / BC + 1);
   }
   auto active = [&](int t) { return !CAUSAL || t * BC <= i0w + 31; };  // wave-uniform
-
-  copy_k(0, 0);
-  copy_v(0, 0);
-  if (n_kv > 1) copy_k(1, 1);
 
   // ---- Q tile -> VGPRs, as the B operand of Sᵀ = K·Qᵀ (column = query row l%32,
   // contraction slots of half g = head dims 16s+8g .. 16s+8g+7).  Rows past Lq read 0.
@@ -254,18 +286,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const u32x4 x = buf_load16(qrs, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2);
     qr[s] = (x & p.q_and) ^ p.q_xor;
   }
+  // K and V tiles 0..NS-2, in the order the loop continues: K t, V t per tile.
+  // (Q above was issued first: vector memory loads complete in issue order, and
+  // the waits below count outstanding loads.)
+  copy_k(0, I0{});
+  copy_v(0, I0{});
+  if (n_kv > 1) {
+    copy_k(1, std::integral_constant<int, 1>{});
+    copy_v(1, std::integral_constant<int, 1>{});
+  }
+  if (n_kv > 2) {
+    copy_k(2, std::integral_constant<int, 2>{});
+    copy_v(2, std::integral_constant<int, 2>{});
+  }
 
-  // per-lane LDS offsets of the MFMA operand reads
-  const int k_off = l32 * KP + 16 * g;  // K row l%32, chunk 2s+g at +32s
+  // per-lane LDS offsets of the MFMA operand reads.  Tile row r sits in block
+  // r % NBLK at position r / NBLK; rows r and r + 8m (m >= 0, r < 8) differ by a
+  // lane-independent offset, which goes into the instruction's immediate.
+  auto row_off = [](int rows, int BS) { return (rows % NBLK) * BS + (rows / NBLK) * 2 * D; };
+  const int k_off = (l32 % NBLK) * KBS + (l32 / NBLK) * 2 * D + 16 * g;  // K row l%32, chunk 2s+g at +32s
   const int gi = lane >> 4, li = lane & 15;
-  const int v_off = (4 * (gi >> 1) + (li >> 2)) * VP + 2 * (16 * (gi & 1) + 4 * (li & 3));
+  const int v_off = (4 * (gi >> 1) + (li >> 2)) * VBS + 2 * (16 * (gi & 1) + 4 * (li & 3));
 
   auto compute_s = [&](const unsigned char* kb_, f32x16 (&S)[KB]) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       S[kb] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) S[kb] = mfma32<DT>(lds_read16(kb_ + k_off + kb * 32 * KP + 32 * s), qr[s], S[kb]);
+      for (int s = 0; s < KS; ++s)
+        S[kb] = mfma32<DT>(lds_read16(kb_ + k_off + row_off(32 * kb, KBS) + 32 * s), qr[s], S[kb]);
     }
   };
 
@@ -275,8 +324,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16{};
 
-  // softmax of tile t (in S) and Oᵀ += Vᵀ·Pᵀ with V from vb_
-  auto softmax_pv = [&](f32x16 (&S)[KB], int t, const unsigned char* vb_) {
+  // Tiles [0, n_full) are visible in full to every row of the workgroup: no
+  // mask, every wave active.  Causal: tile t is full for row i0 iff 64t+63 <= i0.
+  int n_full = Lk / BC;
+  if constexpr (CAUSAL) n_full = min(n_full, (i0 + 1) / BC);
+
+  // mask of a tile crossing the diagonal or the end of the keys (wave-uniform test)
+  auto mask_tile = [&](f32x16(&S)[KB], int t) {
     const int j0 = t * BC;
     const bool need_mask = (CAUSAL && j0 + BC - 1 > i0w) || (j0 + BC > Lk);
     if (need_mask) {
@@ -291,12 +345,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           S[kb][r] = ko >= lim ? NEG_INF : S[kb][r];
         }
     }
+  };
+  // row max of a tile, in log2 units (c > 0)
+  auto row_max = [&](const f32x16(&S)[KB]) {
     float mx = NEG_INF;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
-    const float m_tile = xhalf_max(mx) * c;
+    return xhalf_max(mx) * c;
+  };
+  // Lazy rescale: the running max moves only when the tile's max exceeds it by
+  // more than TAU; then O and both sums are scaled by 2^(m_old - m_new).
+  auto rescale = [&](float m_tile) {
     const bool grow = m_tile > m_run + TAU;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? m_tile : m_run;
@@ -307,8 +368,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) oacc[nb] *= alpha;
     }
-    const float mb = m_run == NEG_INF ? 0.f : m_run;  // no visible key yet: weights stay 0
-    u32x4 pb[KB][2];
+  };
+  // weights of a tile against the running max, and their two row sums.  Every
+  // row sees key 0 in tile 0, so m_run is finite from the first tile on.
+  auto make_p = [&](const f32x16(&S)[KB], u32x4(&pb)[KB][2]) {
+    const float mb = m_run;
     float sf = 0.f, sr = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -325,40 +389,121 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     l_f += sf;
     l_r += sr;
-    // Oᵀ += Vᵀ·Pᵀ: A operand = 8 keys of one head dim, two transposing reads
+  };
+  // Oᵀ += Vᵀ·Pᵀ: A operand = 8 keys of one head dim, two transposing reads
+  auto pv = [&](const u32x4(&pb)[KB][2], const unsigned char* vb_) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const unsigned char* a0 = vb_ + v_off + (32 * kb + 16 * h) * VP + 64 * nb;
-          const u32x2 lo = lds_read_tr(a0);
-          const u32x2 hi = lds_read_tr(a0 + 8 * VP);
+        for (int nb = 0; nb < NB; ++nb) {
+          const unsigned char* a0 = vb_ + v_off + 64 * nb;
+          const u32x2 lo = lds_read_tr(a0 + row_off(32 * kb + 16 * h, VBS));
+          const u32x2 hi = lds_read_tr(a0 + row_off(32 * kb + 16 * h + 8, VBS));
           oacc[nb] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[kb][h], oacc[nb]);
         }
   };
 
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x16 sA[KB], sB[KB];
-  compute_s(kbuf0, sA);  // tile 0 is active for every wave
-  __syncthreads();       // every wave is done with K buffer 0 before it is refilled
-
-  // iteration t: copies K t+2 -> kbuf[t&1], V t+1 -> vbuf[(t+1)&1]; Sᵀ of tile t+1 from
-  // kbuf[(t+1)&1]; softmax + PV of tile t with V from vbuf[t&1].
-  auto iteration = [&](int t, f32x16 (&Sc)[KB], f32x16 (&Sn)[KB], auto PARc) {
-    constexpr int P = decltype(PARc)::value;
-    if (t + 2 < n_kv) copy_k(t + 2, P);
-    if (t + 1 < n_kv) copy_v(t + 1, P ^ 1);
-    if (t + 1 < n_kv && active(t + 1)) compute_s(kbuf0 + (P ^ 1) * KT, Sn);
-    if (active(t)) softmax_pv(Sc, t, vbuf0 + P * VT);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // Waits for all but the newest n of this wave's outstanding vector loads, then
+  // joins the workgroup.  LDS written by the tile copies is visible to every wave
+  // after the barrier once each wave has waited for its own copies.
+  auto wait_join = [&](int n) {
+    switch (n) {
+#define FA355_WAIT(N) \
+  case N: __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14)); break;
+      FA355_WAIT(0) FA355_WAIT(1) FA355_WAIT(2) FA355_WAIT(3) FA355_WAIT(4) FA355_WAIT(5)
+      FA355_WAIT(6) FA355_WAIT(7) FA355_WAIT(8) FA355_WAIT(9) FA355_WAIT(10)
+#undef FA355_WAIT
+      default: __builtin_amdgcn_s_waitcnt(0); break;
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
-  for (int t = 0; t < n_kv; t += 2) {
-    iteration(t, sA, sB, std::integral_constant<int, 0>{});
-    if (t + 1 < n_kv) iteration(t + 1, sB, sA, std::integral_constant<int, 1>{});
+  constexpr int CPW = G::CPW;
+
+  auto kst_rt = [&](int st) -> unsigned char* { return st == 0 ? ks0 : st == 1 ? ks1 : st == 2 ? ks2 : ks3; };
+  auto vst_rt = [&](int st) -> unsigned char* { return st == 0 ? vs0 : st == 1 ? vs1 : st == 2 ? vs2 : vs3; };
+  // K and V of tile t+NS-1, copied in iteration t into stage (t-1) % NS, which
+  // every wave finished with before the last barrier
+  auto copies_rt = [&](int t) {
+    switch ((t + G::NS - 1) % G::NS) {
+      case 0: copy_k(t + G::NS - 1, I0{}); copy_v(t + G::NS - 1, I0{}); break;
+      case 1: copy_k(t + G::NS - 1, std::integral_constant<int, 1>{}); copy_v(t + G::NS - 1, std::integral_constant<int, 1>{}); break;
+      case 2: copy_k(t + G::NS - 1, std::integral_constant<int, 2>{}); copy_v(t + G::NS - 1, std::integral_constant<int, 2>{}); break;
+      default: copy_k(t + G::NS - 1, std::integral_constant<int, 3>{}); copy_v(t + G::NS - 1, std::integral_constant<int, 3>{}); break;
+    }
+  };
+  // End of iteration t: every wave needs K t+2 and V t+1; the loads issued after
+  // them (V t+2, K t+3, V t+3, those that exist) may stay in flight.
+  auto end_iter = [&](int t) { wait_join(CPW * ((t + 2 < n_kv) + 2 * (t + G::NS - 1 < n_kv))); };
+
+  // tile 0's K is in once V0, K1, V1, K2, V2 (those that exist) are the only
+  // loads still outstanding
+  wait_join(CPW * (1 + 2 * (n_kv > 1) + 2 * (n_kv > 2)));
+  f32x16 sA[KB], sB[KB];
+  float mxA = NEG_INF, mxB = NEG_INF;
+  int t_tail = 0;
+  if (n_full > 0) {
+    // ---- full tiles, software-pipelined: iteration t computes Sᵀ of tile t+1
+    // (K stage (t+1) % NS) and its row max while the weights and PV of tile t (V
+    // stage t % NS) run; the rescale for tile t uses the max found one iteration
+    // earlier.  No mask and no branch inside the body.
+    compute_s(kst(I0{}), sA);
+    mxA = row_max(sA);
+    auto it_main = [&](int t, f32x16(&Sc)[KB], f32x16(&Sn)[KB], float& mxc, float& mxn, auto Pc) {
+      constexpr int P = decltype(Pc)::value;
+      using PN = std::integral_constant<int, (P + 1) % G::NS>;
+      using PC = std::integral_constant<int, (P + G::NS - 1) % G::NS>;
+      rescale(mxc);
+      if (t + G::NS - 1 < n_kv) {
+        copy_k(t + G::NS - 1, PC{});
+        copy_v(t + G::NS - 1, PC{});
+      }
+      compute_s(kst(PN{}), Sn);
+      u32x4 pb[KB][2];
+      make_p(Sc, pb);
+      pv(pb, vst(Pc));
+      mxn = row_max(Sn);
+      end_iter(t);
+    };
+    static_assert(G::NS == 4, "the loop below is unrolled over the stages");
+    for (int t = 0; t + 1 < n_full; t += 4) {
+      it_main(t, sA, sB, mxA, mxB, I0{});
+      if (t + 2 < n_full) it_main(t + 1, sB, sA, mxB, mxA, std::integral_constant<int, 1>{});
+      if (t + 3 < n_full) it_main(t + 2, sA, sB, mxA, mxB, std::integral_constant<int, 2>{});
+      if (t + 4 < n_full) it_main(t + 3, sB, sA, mxB, mxA, std::integral_constant<int, 3>{});
+    }
+    // weights and PV of the last full tile, whose Sᵀ is already computed
+    const int tf = n_full - 1;
+    auto finish = [&](f32x16(&Sc)[KB], float mxc) {
+      rescale(mxc);
+      if (tf + G::NS - 1 < n_kv) copies_rt(tf);
+      u32x4 pb[KB][2];
+      make_p(Sc, pb);
+      pv(pb, vst_rt(tf % G::NS));
+      end_iter(tf);
+    };
+    if (tf & 1)
+      finish(sB, mxB);
+    else
+      finish(sA, mxA);
+    t_tail = n_full;
+  }
+  // ---- tiles that cross the diagonal or the end of the keys: not pipelined,
+  // masked; a wave skips tiles above its own rows but still copies and joins.
+  for (int t = t_tail; t < n_kv; ++t) {
+    if (t + G::NS - 1 < n_kv) copies_rt(t);
+    if (active(t)) {
+      compute_s(kst_rt(t % G::NS), sA);
+      mask_tile(sA, t);
+      rescale(row_max(sA));
+      u32x4 pb[KB][2];
+      make_p(sA, pb);
+      pv(pb, vst_rt(t % G::NS));
+    }
+    end_iter(t);
   }
 
   // ---- epilogue: normalise by the sum of the rounded weights, store O and LSE
