@@ -77,6 +77,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   p.Lk = Lk;
   p.n_qt = (int)n_qt;
   p.num_wg = (int)num_wg;
+  p.bh = (int)((int64_t)B * H);
   p.xcd_remap = (num_wg % 8 == 0) ? 1 : 0;
   // The softmax runs in base 2 with the scale folded into one positive factor;
   // a negative scale negates Q (exact in fp16/bf16) and a zero scale zeroes it.

@@ -13,9 +13,9 @@
 //   * K and V tiles of BC keys are copied HBM -> LDS by the buffer unit itself
 //     (buffer_load ... lds, no VGPR staging) into a ring of four stages: the
 //     copies of tile t+3 are issued while tile t is computed ([DF §2.3] prefetch
-//     of the next block, three tiles deep here).  Each iteration waits only for
-//     the tiles it needs next (an explicit vmcnt count) and joins the workgroup
-//     with a bare s_barrier, so later copies stay in flight across iterations;
+//     of the next block, three tiles ahead here).  At the end of an iteration
+//     each wave waits for its own copies (vmcnt) and the workgroup joins with a
+//     bare s_barrier, without the memory fence a __syncthreads would add;
 //   * in LDS, 1 KB copy block b of a tile holds rows b, b+NBLK, b+2·NBLK, ... and
 //     blocks are padded apart: every copy uses one per-lane offset, and the rows
 //     read together by an MFMA operand fall on distinct banks;
@@ -41,7 +41,8 @@
 //     rounded to the input type; lse = (m + log2 l_f)·ln 2 (l_f: fp32 sum).
 // Causal ([DF §4.1] flag): key tiles above a workgroup's last row are never
 // loaded or computed, a wave skips tiles above its own rows, and only tiles that
-// cross the diagonal or the end of the keys pay for the mask.
+// cross the diagonal or the end of the keys pay for the mask.  Causal work items
+// are ordered heads in pairs, heaviest query tiles first within a pair.
 //
 // MFMA 32x32 accumulator layout used throughout: lane l, register r hold
 // C[row = 8*(r/4) + 4*(l/32) + r%4][col = l%32].  A-operand lane l holds row l%32
@@ -88,8 +89,9 @@ struct FwdParams {
   void* o;
   float* lse;
   int Lq, Lk;
-  int n_qt;         // query tiles per head: ceil(Lq / BR)
+  int n_qt;         // query tiles per head: ceil(Lq / 128)
   int num_wg;       // B * H * n_qt
+  int bh;           // B * H
   int xcd_remap;    // 1: group consecutive work items on one XCD
   float c;          // |scale| * log2(e), or log2(e) when scale == 0 (always > 0)
   uint32_t q_and;   // 0xffffffff, or 0 when scale == 0 (Q forced to zero)
@@ -155,6 +157,16 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
 // 32-bit LDS address of a __shared__ object
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// A copy of x that the compiler cannot relate to x: values derived from it are
+// recomputed where they are needed instead of being kept live (and spilled)
+// across the whole kernel.
+__device__ __forceinline__ int opaque(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+  return x;
 }
 
 // max / sum of a value over lanes l and l^32 (every lane gets the result)
@@ -236,8 +248,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // serves the K/V re-reads of that head.
   const int bid = blockIdx.x;
   const int item = p.xcd_remap ? (bid & 7) * (p.num_wg >> 3) + (bid >> 3) : bid;
-  const int bh = item / p.n_qt;
-  const int qt_r = item - bh * p.n_qt;
+  int bh, qt_r;
+  if (CAUSAL) {
+    // Heads in pairs, and within a pair the query tiles of both heads heaviest
+    // first: work is then dispatched nearly longest-first while only two heads'
+    // K/V are streamed at a time on each XCD (an odd last head runs alone).
+    const int g = item / (2 * p.n_qt), j = item - g * 2 * p.n_qt;
+    if (2 * g + 1 < p.bh) {
+      bh = 2 * g + (j & 1);
+      qt_r = j >> 1;
+    } else {
+      bh = 2 * g;
+      qt_r = j;
+    }
+  } else {
+    bh = item / p.n_qt;
+    qt_r = item - bh * p.n_qt;
+  }
+  bh = __builtin_amdgcn_readfirstlane(bh);  // uniform: keep it in scalar registers
+  qt_r = __builtin_amdgcn_readfirstlane(qt_r);
   const int qt = CAUSAL ? p.n_qt - 1 - qt_r : qt_r;
   const int i0 = qt * G::BR;
   const int i0w = i0 + 32 * wave;
@@ -335,8 +364,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool need_mask = (CAUSAL && j0 + BC - 1 > i0w) || (j0 + BC > Lk);
     if (need_mask) {
       // key offset within the tile of S[kb][r] is 32kb + 8(r/4) + 4g + r%4
-      const int lim_tail = Lk - j0 - 4 * g;
-      const int lim = CAUSAL ? min(qrow - j0 - 4 * g + 1, lim_tail) : lim_tail;
+      // (lane-derived values taken afresh, see opaque())
+      const int lane_m = opaque(tid) & 63;
+      const int g_m = lane_m >> 5, row_m = i0w + (lane_m & 31);
+      const int lim_tail = Lk - j0 - 4 * g_m;
+      const int lim = CAUSAL ? min(row_m - j0 - 4 * g_m + 1, lim_tail) : lim_tail;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -355,20 +387,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
     return xhalf_max(mx) * c;
   };
-  // Lazy rescale: the running max moves only when the tile's max exceeds it by
-  // more than TAU; then O and both sums are scaled by 2^(m_old - m_new).
-  auto rescale = [&](float m_tile) {
+  // Lazy rescale: the running max moves only when a tile's max exceeds it by
+  // more than TAU; then both sums and the partial output are scaled by
+  // 2^(m_old - m_new).  In two steps, so that a caller can scale the output after
+  // the tile's weights are made (S is dead by then, which keeps register
+  // pressure down).
+  float alpha = 1.f;
+  auto move_max = [&](float m_tile) -> bool {
     const bool grow = m_tile > m_run + TAU;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
+    const bool any = __builtin_amdgcn_ballot_w64(grow) != 0;
+    if (any) {
       const float m_new = grow ? m_tile : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_f *= alpha;
       l_r *= alpha;
+    }
+    return any;
+  };
+  auto scale_o = [&](bool any) {
+    if (any) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) oacc[nb] *= alpha;
     }
   };
+  auto rescale = [&](float m_tile) { scale_o(move_max(m_tile)); };
   // weights of a tile against the running max, and their two row sums.  Every
   // row sees key 0 in tile 0, so m_run is finite from the first tile on.
   auto make_p = [&](const f32x16(&S)[KB], u32x4(&pb)[KB][2]) {
@@ -405,23 +448,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
   };
 
-  // Waits for all but the newest n of this wave's outstanding vector loads, then
-  // joins the workgroup.  LDS written by the tile copies is visible to every wave
-  // after the barrier once each wave has waited for its own copies.
-  auto wait_join = [&](int n) {
-    switch (n) {
-#define FA355_WAIT(N) \
-  case N: __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14)); break;
-      FA355_WAIT(0) FA355_WAIT(1) FA355_WAIT(2) FA355_WAIT(3) FA355_WAIT(4) FA355_WAIT(5)
-      FA355_WAIT(6) FA355_WAIT(7) FA355_WAIT(8) FA355_WAIT(9) FA355_WAIT(10)
-#undef FA355_WAIT
-      default: __builtin_amdgcn_s_waitcnt(0); break;
-    }
+  // End of a step: every wave waits for its own tile copies, then the workgroup
+  // joins with a bare s_barrier (no memory fence: the copies are ordered by the
+  // explicit vmcnt wait, and the compiler is kept from moving LDS accesses
+  // across).  The copies of a step are issued three tiles ahead of their use and
+  // land well within the step, so waiting for all of them costs nothing.
+  auto wait_join = [&]() {
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  constexpr int CPW = G::CPW;
 
   auto kst_rt = [&](int st) -> unsigned char* { return st == 0 ? ks0 : st == 1 ? ks1 : st == 2 ? ks2 : ks3; };
   auto vst_rt = [&](int st) -> unsigned char* { return st == 0 ? vs0 : st == 1 ? vs1 : st == 2 ? vs2 : vs3; };
@@ -435,13 +472,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       default: copy_k(t + G::NS - 1, std::integral_constant<int, 3>{}); copy_v(t + G::NS - 1, std::integral_constant<int, 3>{}); break;
     }
   };
-  // End of iteration t: every wave needs K t+2 and V t+1; the loads issued after
-  // them (V t+2, K t+3, V t+3, those that exist) may stay in flight.
-  auto end_iter = [&](int t) { wait_join(CPW * ((t + 2 < n_kv) + 2 * (t + G::NS - 1 < n_kv))); };
+  auto end_iter = [&](int) { wait_join(); };
 
-  // tile 0's K is in once V0, K1, V1, K2, V2 (those that exist) are the only
-  // loads still outstanding
-  wait_join(CPW * (1 + 2 * (n_kv > 1) + 2 * (n_kv > 2)));
+  wait_join();  // tiles 0..2 and Q are in
   f32x16 sA[KB], sB[KB];
   float mxA = NEG_INF, mxB = NEG_INF;
   int t_tail = 0;
@@ -497,16 +530,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (t + G::NS - 1 < n_kv) copies_rt(t);
     if (active(t)) {
       compute_s(kst_rt(t % G::NS), sA);
+      // (scheduling barriers: the operand reads of one product are not hoisted
+      // over the softmax, which would run this path out of registers)
+      __builtin_amdgcn_sched_barrier(0);
       mask_tile(sA, t);
-      rescale(row_max(sA));
+      const bool any = move_max(row_max(sA));
       u32x4 pb[KB][2];
       make_p(sA, pb);
+      scale_o(any);
+      __builtin_amdgcn_sched_barrier(0);
       pv(pb, vst_rt(t % G::NS));
     }
     end_iter(t);
   }
 
-  // ---- epilogue: normalise by the sum of the rounded weights, store O and LSE
+  // ---- epilogue: normalise by the sum of the rounded weights, store O and LSE.
+  // The lane's row and half are derived afresh (see opaque()).
+  const int lane_e = opaque(tid) & 63;
+  const int g_e = lane_e >> 5, row_e = i0w + (lane_e & 31);
   const float lf_t = xhalf_sum(l_f);
   const float lr_t = xhalf_sum(l_r);
   const float inv = 1.0f / lr_t;
@@ -514,12 +555,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = 32 * nb + 8 * q4 + 4 * g;
+      const int d0 = 32 * nb + 8 * q4 + 4 * g_e;
       const u32x2 w = {pack2<DT>(oacc[nb][4 * q4] * inv, oacc[nb][4 * q4 + 1] * inv),
                        pack2<DT>(oacc[nb][4 * q4 + 2] * inv, oacc[nb][4 * q4 + 3] * inv)};
-      buf_store8(ors, (uint32_t)(qrow * D + d0) * 2, w);  // rows >= Lq are dropped
+      buf_store8(ors, (uint32_t)(row_e * D + d0) * 2, w);  // rows >= Lq are dropped
     }
-  if (g == 0 && qrow < Lq) p.lse[(size_t)bh * Lq + qrow] = (m_run + log2f(lf_t)) * 0.69314718055994530942f;
+  if (g_e == 0 && row_e < Lq) p.lse[(size_t)bh * Lq + row_e] = (m_run + log2f(lf_t)) * 0.69314718055994530942f;
 }
 
 }  // namespace fa355
