@@ -33,6 +33,8 @@
 #ifndef FA355_H
 #define FA355_H
 
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -56,7 +58,8 @@ typedef enum {
   FA_ERR_SCALE = -6,        /* scale is NaN or infinite                                          */
   FA_ERR_CAUSAL_SHAPE = -7, /* causal with Lq != Lk (the alignment of such a mask is undefined)  */
   FA_ERR_DEVICE = -8,       /* the current device has no gfx950 code object for the kernel       */
-  FA_ERR_LAUNCH = -9        /* the kernel launch failed (HIP code in fa_last_hip_error())        */
+  FA_ERR_LAUNCH = -9,       /* the kernel launch failed (HIP code in fa_last_hip_error())        */
+  FA_ERR_STRIDE = -10       /* fa_fwd_strided: a stride < 0, or a row stride < D                 */
 } fa_status;
 
 /*
@@ -77,8 +80,8 @@ typedef enum {
  *   dtype               FA_DTYPE_F16 or FA_DTYPE_BF16 (q, k, v and o share it).
  *   stream              HIP stream to enqueue on.
  *
- * Limits: Lq*D*2 + 256*D*2 and Lk*D*2 + 256*D*2 must stay below 2^32 bytes
- * (one head's slab is addressed with 32-bit offsets, e.g. Lk < 16,777,000 at
+ * Limits: ((L + 256)*D + D)*2 must stay below 2^32 bytes for L = Lq and L = Lk
+ * (one head's slab is addressed with 32-bit offsets: L < 16,776,959 at
  * D = 128), and B*H*ceil(Lq/256) < 2^22 workgroups.
  *
  * Semantics: validation happens on the host before any HIP call; an invalid
@@ -92,6 +95,31 @@ typedef enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Lq, int Lk, int D, float scale, int causal, int dtype,
            fa_stream_t stream);
+
+/*
+ * fa_fwd_strided — fa_fwd on strided views: the same operation, result and
+ * semantics, with q, k, v and o given by element strides instead of the dense
+ * [B, H, L, D] layout, so that [B, L, H, D] tensors and a packed qkv buffer of
+ * shape [B, L, 3, H, D] are used in place, with no copies.  These are the call
+ * forms the pages' interfaces take ([DF §4.1], attention on (batch, sequence,
+ * heads, head-dim) tensors; [AI §4.2], the packed-qkv call).
+ *
+ * Element (b, h, i, d) of q is at q + (b*q_stride[0] + h*q_stride[1] +
+ * i*q_stride[2] + d) elements; likewise k, v (rows 0..Lk-1) and o.  Each
+ * *_stride points to three int64 values in host memory, read during the call
+ * only.  The head dim is contiguous.  lse stays dense [B, H, Lq] fp32.
+ *
+ * Extra checks, before any HIP call: the stride pointers are non-NULL
+ * (FA_ERR_NULL); every stride is >= 0 and every row stride >= D (FA_ERR_STRIDE;
+ * batch or head strides of 0 broadcast one slab, e.g. K/V shared by all heads);
+ * every stride is a multiple of 8 elements, so that each row starts on a 16-byte
+ * boundary (FA_ERR_ALIGN); ((L + 256)*row_stride + D)*2 < 2^32 for each tensor
+ * (FA_ERR_SHAPE).  Rows of o must not overlap each other or q, k, v (not
+ * checked).  fa_fwd is this call with the dense strides.
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+                   int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                   const int64_t* o_stride, float scale, int causal, int dtype, fa_stream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -36,8 +36,20 @@ def call(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, Lq=64, Lk=64, D=128
     return fa.lib.fa_fwd(q, k, v, o, lse, B, H, Lq, Lk, D, scale, causal, dtype, None)
 
 
+def call_strided(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, Lq=64, Lk=64, D=128, strides=None,
+                 scale=0.125, causal=0, dtype=1):
+    """fa_fwd_strided with per-tensor (batch, head, row) strides; default: [B, L, H, D] views."""
+    dflt = {"q": (Lq * H * D, D, H * D), "k": (Lk * H * D, D, H * D), "v": (Lk * H * D, D, H * D),
+            "o": (Lq * H * D, D, H * D)}
+    dflt.update(strides or {})
+    arr = {n: (None if s_ is None else (ctypes.c_int64 * 3)(*s_)) for n, s_ in dflt.items()}
+    ptr = [None if arr[n] is None else ctypes.cast(arr[n], ctypes.c_void_p) for n in ("q", "k", "v", "o")]
+    return fa.lib.fa_fwd_strided(q, k, v, o, lse, B, H, Lq, Lk, D, *ptr, scale, causal, dtype, None)
+
+
 def test_header_declares_the_abi():
-    assert declared_functions() == ["fa_fwd", "fa_status_string", "fa_last_hip_error", "fa_version"]
+    assert declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_status_string", "fa_last_hip_error",
+                                    "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -52,8 +64,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert fa.fa_version() == 10000
-    for code in range(0, -10, -1):
+    assert fa.fa_version() == 10100
+    for code in range(0, -11, -1):
         s = fa.fa_status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in fa.fa_status_string(5)
@@ -111,6 +123,44 @@ def test_causal_requires_square():
     assert call(causal=7, Lq=3, Lk=2) == -7
 
 
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_strided_null_stride_pointer(which):
+    assert call_strided(strides={which: None}) == -1
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+@pytest.mark.parametrize("bad", [(-8, 128, 384), (0, -128, 384), (0, 0, 120), (0, 0, -8)])
+def test_strided_bad_strides(which, bad):
+    # negative strides, or a row stride below D (rows would overlap)
+    assert call_strided(strides={which: bad}) == -10
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+@pytest.mark.parametrize("bad", [(12, 128, 384), (0, 4, 384), (0, 0, 129)])
+def test_strided_misaligned_strides(which, bad):
+    # every row must start on a 16-byte boundary: strides are multiples of 8 elements
+    assert call_strided(strides={which: bad}) == -5
+
+
+@pytest.mark.parametrize("which", ["q", "k", "o"])
+def test_strided_row_stride_limit(which):
+    # ((L + 256) * row_stride + D) * 2 must stay below 2^32
+    assert call_strided(strides={which: (0, 0, 1 << 24)}) == -2
+
+
+def test_strided_valid_strides_reach_later_checks():
+    # broadcast K/V (batch and head stride 0) and padded rows are accepted; a later
+    # check (head dim) fails, so nothing launches
+    assert call_strided(strides={"k": (0, 0, 136), "v": (0, 0, 256)}, D=96) == -3
+    assert call_strided(causal=1, Lq=64, Lk=65) == -7
+    assert call_strided(scale=float("nan")) == -6
+
+
+def test_dense_call_matches_the_strided_checks():
+    # fa_fwd is fa_fwd_strided with dense strides: same codes for the same faults
+    assert call(Lk=16_776_960) == call_strided(Lk=16_776_960, strides={"k": (0, 0, 128), "v": (0, 0, 128)}) == -2
+
+
 def test_python_binding_rejects_bad_tensors():
     import torch
 
@@ -123,6 +173,11 @@ def test_python_binding_rejects_bad_tensors():
         fa.fa_fwd(q[0], q[0], q[0])             # not 4-D
     with pytest.raises(ValueError):
         fa.fa_fwd(q, q[:, :, :2], q)            # k/v mismatch
+    qt = torch.zeros(1, 1, 64, 4, dtype=torch.float16).transpose(2, 3)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(qt, qt, qt)                   # head dim not contiguous
+    with pytest.raises(ValueError):
+        fa.fa_fwd_qkvpacked(torch.zeros(1, 4, 2, 1, 64, dtype=torch.float16))  # not [B, L, 3, H, D]
 
 
 def test_missing_library_fails_loudly(tmp_path):

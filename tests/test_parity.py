@@ -240,3 +240,90 @@ def test_outputs_written_into_given_buffers():
     torch.cuda.synchronize()
     assert o2.data_ptr() == o.data_ptr() and lse2.data_ptr() == lse.data_ptr()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+# ------------------------------------------------------------------------------------------
+# strided and packed layouts (fa_fwd_strided): the same results on views of other layouts
+# ------------------------------------------------------------------------------------------
+
+def _views(layout, inp, pad=64):
+    """GPU views of q, k, v and an output view o in the requested layout, plus a check of o's padding."""
+    q, k, v = (inp[n] for n in ("q", "k", "v"))
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    blhd = lambda t: t.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)   # [B,L,H,D] storage, [B,H,L,D] view
+    if layout == "blhd":
+        o_buf = torch.full((B, Lq, H, D), float("nan"), dtype=q.dtype, device=DEV)
+        return blhd(q), blhd(k), blhd(v), o_buf.transpose(1, 2), None
+    if layout == "padded":
+        def padded(t):
+            buf = torch.zeros(t.shape[0], t.shape[1] + 1, t.shape[2], t.shape[3] + pad, dtype=t.dtype)
+            buf[:, :-1, :, :D] = t
+            return buf.to(DEV)[:, :-1, :, :D]
+        o_buf = torch.full((B, H + 1, Lq, D + pad), 7.0, dtype=q.dtype, device=DEV)
+        o = o_buf[:, :-1, :, :D]
+        def untouched():
+            assert bool((o_buf[:, -1] == 7).all()) and bool((o_buf[..., D:] == 7).all()), "padding of o written"
+        return padded(q), padded(k), padded(v), o, untouched
+    if layout == "broadcast_kv":
+        # one K/V slab shared by every batch and head: zero batch and head strides
+        k1, v1 = k[:1, :1].to(DEV), v[:1, :1].to(DEV)
+        return q.to(DEV), k1.expand(B, H, Lk, D), v1.expand(B, H, Lk, D), None, None
+    if layout == "mixed":
+        o_buf = torch.full((B, Lq, H, D + 8), float("nan"), dtype=q.dtype, device=DEV)
+        return q.to(DEV), blhd(k), blhd(v), o_buf[..., :D].transpose(1, 2), None
+    raise ValueError(layout)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "fp16")])
+@pytest.mark.parametrize("layout", ["blhd", "padded", "broadcast_kv", "mixed"])
+def test_strided_layouts(layout, D, dtype, causal):
+    inp = ai.make_custom(2, 3, 300, 300, D, dtype, causal, seed=700 + D + (1 if causal else 0))
+    note(f"strided {layout} D{D} {dtype} causal={causal}")
+    q, k, v, o, check = _views(layout, inp)
+    o, lse = fa.fa_fwd(q, k, v, o, causal=causal, scale=inp["scale"])
+    torch.cuda.synchronize()
+    kd, vd = k.cpu().contiguous(), v.cpu().contiguous()          # the dense tensors the views show
+    O_ref, L_ref = attention_fp64(q.cpu().contiguous(), kd, vd, inp["scale"], causal)
+    compare(o.cpu().contiguous(), lse, O_ref, L_ref, dtype, f"strided {layout}")
+    if check:
+        check()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "fp16")])
+def test_qkvpacked(D, dtype, causal):
+    inp = ai.make_custom(2, 3, 333, 333, D, dtype, causal, seed=800 + D)
+    note(f"qkvpacked D{D} {dtype} causal={causal}")
+    qkv = torch.stack([inp[n].transpose(1, 2) for n in ("q", "k", "v")], dim=2).contiguous().to(DEV)  # [B,L,3,H,D]
+    o, lse = fa.fa_fwd_qkvpacked(qkv, causal=causal, scale=inp["scale"])
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (2, 333, 3, D)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], causal)
+    compare(o.transpose(1, 2).cpu().contiguous(), lse, O_ref, L_ref, dtype, "qkvpacked")
+
+
+def test_strided_matches_dense_bitwise():
+    # the same values through fa_fwd (dense) and fa_fwd_strided on [B,L,H,D] storage give the same bits
+    inp = ai.make_custom(1, 4, 700, 700, 128, "bf16", True, seed=901)
+    o1, l1 = run_gpu(inp)
+    q, k, v, o, _ = _views("blhd", inp)
+    o2, l2 = fa.fa_fwd_strided(q, k, v, o, causal=True, scale=inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.cpu(), o2.cpu()) and torch.equal(l1.cpu(), l2.cpu())
+
+
+def test_strided_train_shape_sampled():
+    # the 7B 4K training shape in [B, L, H, D] storage, sampled rows against the oracle
+    w = ai.WORKLOADS["train7b_4k"]
+    inp = ai.make_inputs(w)
+    note("strided train7b_4k in [B,L,H,D] storage")
+    q, k, v, o, _ = _views("blhd", inp)
+    o, lse = fa.fa_fwd(q, k, v, o, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    heads, rows = _sample(w, seed=3)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, True, rows=rows, heads=heads)
+    oc, lc = o.cpu(), lse.cpu()
+    for b, h in heads:
+        compare(oc[b, h][rows], lc[b, h][rows], O_ref[b, h], L_ref[b, h], w.dtype, f"strided train ({b},{h})")

@@ -5,8 +5,9 @@ kernel behind the C ABI declared in ``include/fa355.h``.  PyTorch supplies
 device memory and the current stream.  There is no fallback: if the compiled
 library is missing, importing this package raises ImportError.
 
-Names follow the C ABI: ``fa_fwd``, ``fa_status_string``, ``fa_last_hip_error``,
-``fa_version``.
+Names follow the C ABI: ``fa_fwd``, ``fa_fwd_strided``, ``fa_status_string``,
+``fa_last_hip_error``, ``fa_version``; ``fa_fwd_qkvpacked`` is a view helper over
+``fa_fwd_strided`` for a packed [B, L, 3, H, D] qkv buffer.
 """
 
 from __future__ import annotations
@@ -17,7 +18,7 @@ import os
 
 import torch
 
-__all__ = ["fa_fwd", "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH",
+__all__ = ["fa_fwd", "fa_fwd_strided", "fa_fwd_qkvpacked", "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH",
            "FA_DTYPE_F16", "FA_DTYPE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
@@ -36,6 +37,8 @@ def _load() -> ctypes.CDLL:
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float, i, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, ctypes.c_float, i, i, vp]
+    lib.fa_fwd_strided.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -66,17 +69,9 @@ def fa_version() -> int:
     return int(lib.fa_version())
 
 
-def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
-           lse: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
-           stream: torch.cuda.Stream | None = None):
-    """Enqueue ``fa_fwd`` on ``stream`` (default: torch's current stream of q's device).
-
-    q: [B, H, Lq, D]; k, v: [B, H, Lk, D]; contiguous fp16/bf16 tensors on one GPU.
-    o ([B, H, Lq, D], q's dtype) and lse ([B, H, Lq], float32) are allocated when
-    not given.  ``scale`` defaults to 1/sqrt(D).  Returns (o, lse).
-    """
+def _check(q, k, v, o, lse):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-D [B, H, L, D]")
+        raise ValueError("q, k, v must be 4-D [B, H, L, D] (views of any strides)")
     B, H, Lq, D = q.shape
     Lk = k.shape[2]
     if tuple(k.shape) != (B, H, Lk, D) or tuple(v.shape) != (B, H, Lk, D):
@@ -86,23 +81,78 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | 
     dev = q.device
     if dev.type != "cuda" or k.device != dev or v.device != dev:
         raise ValueError("q, k, v must be on the same GPU")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     if o is None:
-        o = torch.empty_like(q)
-    elif o.shape != q.shape or o.dtype != q.dtype or o.device != dev or not o.is_contiguous():
-        raise ValueError("o must be a contiguous tensor like q")
+        o = torch.empty_like(q, memory_format=torch.contiguous_format)
+    elif tuple(o.shape) != tuple(q.shape) or o.dtype != q.dtype or o.device != dev:
+        raise ValueError("o must be a tensor of q's shape, dtype and device")
     if lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
     elif tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or lse.device != dev or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [B, H, Lq]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}: the head dim must be contiguous (stride 1)")
+    return B, H, Lq, Lk, D, o, lse
+
+
+def _launch(strided, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream):
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    code = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                      B, H, Lq, Lk, D, float(scale), 1 if causal else 0, _DTYPES[q.dtype], stream.cuda_stream)
+        stream = torch.cuda.current_stream(q.device)
+    if not strided:
+        code = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, H, Lq, Lk, D, float(scale), 1 if causal else 0, _DTYPES[q.dtype], stream.cuda_stream)
+    else:
+        st = [(ctypes.c_int64 * 3)(*t.stride()[:3]) for t in (q, k, v, o)]
+        code = lib.fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, H, Lq, Lk, D, *[ctypes.cast(s_, ctypes.c_void_p) for s_ in st],
+                                  float(scale), 1 if causal else 0, _DTYPES[q.dtype], stream.cuda_stream)
     if code != 0:
         raise FaError(code)
+    return o, lse
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
+           lse: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
+           stream: torch.cuda.Stream | None = None):
+    """Enqueue the attention forward pass on ``stream`` (default: torch's current stream of q's device).
+
+    q: [B, H, Lq, D]; k, v: [B, H, Lk, D]; fp16/bf16 tensors on one GPU, dense or
+    any strided views with a contiguous head dim (a [B, L, H, D] tensor passed as
+    ``x.transpose(1, 2)`` is used in place).  o (q's shape and dtype, dense or a
+    view) and lse ([B, H, Lq], float32, dense) are allocated when not given.
+    ``scale`` defaults to 1/sqrt(D).  Dense inputs go through the C ``fa_fwd``,
+    others through ``fa_fwd_strided``.  Returns (o, lse).
+    """
+    B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
+    dense = all(t.is_contiguous() for t in (q, k, v, o))
+    return _launch(not dense, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream)
+
+
+def fa_fwd_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
+                   stream: torch.cuda.Stream | None = None):
+    """Like ``fa_fwd``, always through the C ``fa_fwd_strided`` (the tensors' own strides)."""
+    B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
+    return _launch(True, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream)
+
+
+def fa_fwd_qkvpacked(qkv: torch.Tensor, o: torch.Tensor | None = None, lse: torch.Tensor | None = None, *,
+                     causal: bool = False, scale: float | None = None, stream: torch.cuda.Stream | None = None):
+    """Attention on a packed qkv buffer [B, L, 3, H, D] (q, k, v interleaved per position).
+
+    Runs in place on strided views of qkv.  o, when not given, is allocated as
+    [B, L, H, D] (the packed call's output layout); lse is [B, H, L].  Returns
+    (o, lse) with o in [B, L, H, D].
+    """
+    if qkv.dim() != 5 or qkv.shape[2] != 3:
+        raise ValueError("qkv must be [B, L, 3, H, D]")
+    B, L, _, H, D = qkv.shape
+    q, k, v = (qkv[:, :, i].transpose(1, 2) for i in range(3))
+    if o is None:
+        o = torch.empty((B, L, H, D), dtype=qkv.dtype, device=qkv.device)
+    elif tuple(o.shape) != (B, L, H, D):
+        raise ValueError("o must be [B, L, H, D]")
+    _, lse = fa_fwd_strided(q, k, v, o.transpose(1, 2), lse, causal=causal, scale=scale, stream=stream)
     return o, lse

@@ -18,7 +18,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 
 template <int D, int DT, bool CAUSAL>
 int launch(const fa355::FwdParams& p, hipStream_t stream) {
@@ -46,22 +46,28 @@ bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) =
 
 extern "C" {
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk, int D,
-           float scale, int causal, int dtype, fa_stream_t stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+                   int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                   const int64_t* o_stride, float scale, int causal, int dtype, fa_stream_t stream) {
+  if (!q || !k || !v || !o || !lse || !q_stride || !k_stride || !v_stride || !o_stride) return FA_ERR_NULL;
   if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  const int64_t* st[4] = {q_stride, k_stride, v_stride, o_stride};
+  for (int i = 0; i < 4; ++i)
+    if (st[i][0] < 0 || st[i][1] < 0 || st[i][2] < D) return FA_ERR_STRIDE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_ALIGN;
+  for (int i = 0; i < 4; ++i)  // every row starts on a 16-byte boundary
+    if (st[i][0] % 8 || st[i][1] % 8 || st[i][2] % 8) return FA_ERR_ALIGN;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (causal && Lq != Lk) return FA_ERR_CAUSAL_SHAPE;
 
   // One head's slab is addressed with 32-bit byte offsets, including up to 256
-  // rows of tile padding past its end.
-  const uint64_t row_bytes = (uint64_t)D * 2;
-  if (((uint64_t)Lq + 256) * row_bytes >= (1ull << 32) || ((uint64_t)Lk + 256) * row_bytes >= (1ull << 32))
-    return FA_ERR_SHAPE;
+  // rows of tile padding past its end; batch and head offsets are 64-bit.
+  const int64_t lens[4] = {Lq, Lk, Lk, Lq};
+  for (int i = 0; i < 4; ++i)
+    if (((lens[i] + 256) * st[i][2] + D) * 2 >= (1ll << 32)) return FA_ERR_SHAPE;
   const int BR = D == 128 ? fa355::Geo<128>::BR : fa355::Geo<64>::BR;
   const int64_t n_qt = ((int64_t)Lq + BR - 1) / BR;
   const int64_t num_wg = (int64_t)B * H * n_qt;
@@ -75,6 +81,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   p.lse = lse;
   p.Lq = Lq;
   p.Lk = Lk;
+  p.H = H;
+  p.q_sb = q_stride[0], p.q_sh = q_stride[1], p.q_sl = (int)q_stride[2];
+  p.k_sb = k_stride[0], p.k_sh = k_stride[1], p.k_sl = (int)k_stride[2];
+  p.v_sb = v_stride[0], p.v_sh = v_stride[1], p.v_sl = (int)v_stride[2];
+  p.o_sb = o_stride[0], p.o_sh = o_stride[1], p.o_sl = (int)o_stride[2];
   p.n_qt = (int)n_qt;
   p.num_wg = (int)num_wg;
   p.bh = (int)((int64_t)B * H);
@@ -90,6 +101,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return D == 128 ? dispatch_dtype<128>(p, dtype, causal != 0, s) : dispatch_dtype<64>(p, dtype, causal != 0, s);
 }
 
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk, int D,
+           float scale, int causal, int dtype, fa_stream_t stream) {
+  // dense [B, H, L, D]: the strided form with the natural strides
+  const int64_t sq[3] = {(int64_t)H * Lq * D, (int64_t)Lq * D, D};
+  const int64_t sk[3] = {(int64_t)H * Lk * D, (int64_t)Lk * D, D};
+  return fa_fwd_strided(q, k, v, o, lse, B, H, Lq, Lk, D, sq, sk, sk, sq, scale, causal, dtype, stream);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -102,6 +121,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_CAUSAL_SHAPE: return "fa_fwd: causal attention requires Lq == Lk";
     case FA_ERR_DEVICE: return "fa_fwd: no gfx950 kernel for the current device";
     case FA_ERR_LAUNCH: return "fa_fwd: kernel launch failed (see fa_last_hip_error)";
+    case FA_ERR_STRIDE: return "fa_fwd: strides must be >= 0, with a row stride of at least D";
     default: return "fa_fwd: unknown status code";
   }
 }

@@ -89,7 +89,11 @@ struct FwdParams {
   void* o;
   float* lse;
   int Lq, Lk;
-  int n_qt;         // query tiles per head: ceil(Lq / 128)
+  int H;            // heads (b = bh / H, h = bh % H)
+  // element strides of batch, head and row; the head dim is contiguous
+  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int q_sl, k_sl, v_sl, o_sl;
+  int n_qt;         // query tiles per head: ceil(Lq / BR)
   int num_wg;       // B * H * n_qt
   int bh;           // B * H
   int xcd_remap;    // 1: group consecutive work items on one XCD
@@ -142,15 +146,34 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t of
 }
 
 // One 16-byte-per-lane HBM -> LDS copy (buffer_load_dwordx4 ... lds): lane l's
-// 16 bytes land at LDS byte lds + 16·l.  Written as inline assembly so that the
-// compiler neither tracks nor waits for these LDS writes: the kernel orders them
-// itself with explicit vmcnt waits and barriers.  rsrc and lds must be uniform.
+// 16 bytes land at LDS byte lds + 16·l (M0 holds the LDS base; the asm declares
+// M0 as an output, so the compiler knows it changes).  Written as inline
+// assembly so that the compiler neither tracks nor waits for these LDS writes:
+// the kernel orders them itself with explicit vmcnt waits and barriers.  rsrc and
+// lds must be uniform.
 __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
+  uint32_t m0v;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+               : "={m0}"(m0v)
                : "s"(lds), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+               : "memory");
+#endif
+}
+// Two such copies in one statement.
+__device__ __forceinline__ void dma16x2(u32x4 rsrc, uint32_t lds0, uint32_t voff0, uint32_t lds1, uint32_t voff1) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t m0v;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen lds\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %4, %5, 0 offen lds"
+      : "={m0}"(m0v)
+      : "s"(lds0), "v"(voff0), "s"(lds1), "v"(voff1), "s"(rsrc)
+      : "memory");
 #endif
 }
 
@@ -272,31 +295,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int i0w = i0 + 32 * wave;
   const int Lq = p.Lq, Lk = p.Lk;
 
-  const size_t qbase = (size_t)bh * (size_t)Lq * D * 2;
-  const size_t kbase = (size_t)bh * (size_t)Lk * D * 2;
-  const auto qrs = make_rsrc((const char*)p.q + qbase, (uint32_t)Lq * D * 2);
-  const auto ors = make_rsrc((char*)p.o + qbase, (uint32_t)Lq * D * 2);
+  // (batch, head) slabs; a slab's rows are q_sl (k_sl, ...) elements apart and its
+  // buffer range ends with the last row, so rows past the end read 0 / drop stores
+  const int bb = __builtin_amdgcn_readfirstlane(bh / p.H), hh = bh - bb * p.H;
+  const int q_sl = p.q_sl, k_sl = p.k_sl, v_sl = p.v_sl, o_sl = p.o_sl;
+  const char* const qslab = (const char*)p.q + ((int64_t)bb * p.q_sb + (int64_t)hh * p.q_sh) * 2;
+  const char* const kslab = (const char*)p.k + ((int64_t)bb * p.k_sb + (int64_t)hh * p.k_sh) * 2;
+  const char* const vslab = (const char*)p.v + ((int64_t)bb * p.v_sb + (int64_t)hh * p.v_sh) * 2;
+  char* const oslab = (char*)p.o + ((int64_t)bb * p.o_sb + (int64_t)hh * p.o_sh) * 2;
+  const auto qrs = make_rsrc(qslab, (uint32_t)((Lq - 1) * q_sl + D) * 2);
+  const auto ors = make_rsrc(oslab, (uint32_t)((Lq - 1) * o_sl + D) * 2);
 
   // ---- HBM -> LDS copy of one tile.  Copy j of wave w fills block b = w + NW·j:
   // lane l brings the 16-byte chunk l % NCH of tile row b + NBLK·(l / NCH).  The
-  // buffer resource starts at the tile's first key and ends at the last key, so
-  // keys >= Lk read 0; the per-lane offset is the same for every tile.
-  const uint32_t lane_src = (uint32_t)((wave + NBLK * (lane / NCH)) * D * 2 + 16 * (lane % NCH));
-  const char* const kslab = (const char*)p.k + kbase;
-  const char* const vslab = (const char*)p.v + kbase;
-  auto copy_tile = [&](const char* slab, unsigned char* dst, int key0, auto BSc) {
+  // buffer resource starts at the tile's first key and ends with the last key's
+  // row, so keys >= Lk read 0; the per-lane offset is the same for every tile.
+  const int lrow = wave + NBLK * (lane / NCH), lchunk = 16 * (lane % NCH);
+  const uint32_t src_k = (uint32_t)(lrow * k_sl * 2 + lchunk), src_v = (uint32_t)(lrow * v_sl * 2 + lchunk);
+  // per tensor: bytes per tile of BC rows, bytes from the slab start to the end of
+  // its last row, and the offset between a wave's copies
+  const int64_t tb_k = (int64_t)BC * k_sl * 2, tb_v = (int64_t)BC * v_sl * 2;
+  const uint32_t end_k = (uint32_t)((Lk - 1) * k_sl + D) * 2, end_v = (uint32_t)((Lk - 1) * v_sl + D) * 2;
+  const uint32_t step_k = (uint32_t)(G::NW * k_sl * 2), step_v = (uint32_t)(G::NW * v_sl * 2);
+  auto copy_tile = [&](const char* slab, int64_t tb, uint32_t end, uint32_t step, uint32_t lane_src,
+                       unsigned char* dst, int tile, auto BSc) {
     constexpr int BS = decltype(BSc)::value;
-    const uint64_t base = (uint64_t)(uintptr_t)(slab + (size_t)key0 * D * 2);
+    const int64_t off = (int64_t)tile * tb;
+    const uint64_t base = (uint64_t)(uintptr_t)(slab + off);
     const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xffffu)),
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(Lk - key0) * D * 2)),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(end - (uint32_t)off)),
                       (uint32_t)kBufferFlags};
     const uint32_t l0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_addr(dst) + BS * wave));
+    if constexpr (G::CPW == 2)
+      dma16x2(rs, l0, lane_src, l0 + BS * G::NW, lane_src + step);
+    else
 #pragma unroll
-    for (int j = 0; j < G::CPW; ++j) dma16(rs, l0 + BS * G::NW * j, lane_src + G::NW * j * D * 2);
+      for (int j = 0; j < G::CPW; ++j) dma16(rs, l0 + BS * G::NW * j, lane_src + step * j);
   };
-  auto copy_k = [&](int tile, auto Sc) { copy_tile(kslab, kst(Sc), tile * BC, std::integral_constant<int, KBS>{}); };
-  auto copy_v = [&](int tile, auto Sc) { copy_tile(vslab, vst(Sc), tile * BC, std::integral_constant<int, VBS>{}); };
+  auto copy_k = [&](int tile, auto Sc) {
+    copy_tile(kslab, tb_k, end_k, step_k, src_k, kst(Sc), tile, std::integral_constant<int, KBS>{});
+  };
+  auto copy_v = [&](int tile, auto Sc) {
+    copy_tile(vslab, tb_v, end_v, step_v, src_v, vst(Sc), tile, std::integral_constant<int, VBS>{});
+  };
 
   // ---- key range of this workgroup
   int n_kv = (Lk + BC - 1) / BC;
@@ -312,12 +354,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   u32x4 qr[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const u32x4 x = buf_load16(qrs, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2);
+    const u32x4 x = buf_load16(qrs, (uint32_t)(qrow * q_sl + 16 * s + 8 * g) * 2);
     qr[s] = (x & p.q_and) ^ p.q_xor;
   }
   // K and V tiles 0..NS-2, in the order the loop continues: K t, V t per tile.
-  // (Q above was issued first: vector memory loads complete in issue order, and
-  // the waits below count outstanding loads.)
   copy_k(0, I0{});
   copy_v(0, I0{});
   if (n_kv > 1) {
@@ -558,7 +598,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int d0 = 32 * nb + 8 * q4 + 4 * g_e;
       const u32x2 w = {pack2<DT>(oacc[nb][4 * q4] * inv, oacc[nb][4 * q4 + 1] * inv),
                        pack2<DT>(oacc[nb][4 * q4 + 2] * inv, oacc[nb][4 * q4 + 3] * inv)};
-      buf_store8(ors, (uint32_t)(row_e * D + d0) * 2, w);  // rows >= Lq are dropped
+      buf_store8(ors, (uint32_t)(row_e * o_sl + d0) * 2, w);  // rows >= Lq are dropped
     }
   if (g_e == 0 && row_e < Lq) p.lse[(size_t)bh * Lq + row_e] = (m_run + log2f(lf_t)) * 0.69314718055994530942f;
 }
