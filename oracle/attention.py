@@ -22,11 +22,14 @@ oracle is the plain definition, not the tiled algorithm:
     layer).  The per-row log-sum-exp returned here is those two numbers folded
     into one: LSE = max + ln(sum_exp), in natural-log units of the scaled logits.
   * [DF §4.1] the ``causal=True`` flag: key j is visible to query row i iff
-    j <= i (reading taken: diagonal included, Lq == Lk; causal with Lq != Lk is
-    rejected because the pages never define its alignment).
+    j <= i (reading taken: diagonal included).  The pages never define the flag
+    for Lq != Lk; the reading taken there is bottom-right alignment — the Lq
+    query rows are the last Lq positions of the Lk keys, so j is visible to i iff
+    j <= i + (Lk - Lq) — for Lq < Lk (every row still sees key 0), and Lq > Lk
+    is rejected (rows with no visible key would have no softmax).
 
 For every (b, h, i), with inputs upcast exactly to fp64:
-  A_i   = {0..Lk-1}, or {0..i} when causal
+  A_i   = {0..Lk-1}, or {0..i + Lk - Lq} when causal
   s_ij  = scale * sum_d q[b,h,i,d] * k[b,h,j,d]           for j in A_i
   m_i   = max_{j in A_i} s_ij
   p_ij  = exp(s_ij - m_i),  l_i = sum_{j in A_i} p_ij
@@ -71,8 +74,9 @@ def attention_head_fp64(q, k, v, scale: float, causal: bool, rows=None, chunk: i
     Lk = k.shape[0]
     if k.shape != (Lk, D) or v.shape[0] != Lk:
         raise ValueError("k must be [Lk, D] and v must be [Lk, Dv]")
-    if causal and Lq != Lk:
-        raise ValueError("causal attention is defined here only for Lq == Lk")
+    if causal and Lq > Lk:
+        raise ValueError("causal attention is defined here only for Lq <= Lk (bottom-right alignment)")
+    off = Lk - Lq  # causal: query row i sits at key position i + off
     rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
     R = rows.shape[0]
     O = np.empty((R, v.shape[1]), dtype=np.float64)
@@ -83,8 +87,8 @@ def attention_head_fp64(q, k, v, scale: float, causal: bool, rows=None, chunk: i
         # stage 1: scores of the selected rows against every key ([OP §2.1], [DF §2.1])
         S = (q[r] @ kT) * scale
         if causal:
-            # [DF §4.1] causal flag; reading: key j visible to row i iff j <= i
-            S[np.arange(Lk)[None, :] > r[:, None]] = -np.inf
+            # [DF §4.1] causal flag; reading: key j visible to row i iff j <= i + (Lk - Lq)
+            S[np.arange(Lk)[None, :] > r[:, None] + off] = -np.inf
         # stage 2: softmax as max, exp, row sum ([DF §2.1] stage 2, [DF §2.2] second layer)
         m = S.max(axis=1)
         P = np.exp(S - m[:, None])

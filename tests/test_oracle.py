@@ -258,8 +258,45 @@ def pin_scale_homogeneity(attn):
     np.testing.assert_allclose(L3, math.log(9), atol=1e-14)
 
 
+def pin_causal_bottom_right(attn):
+    """Causal with Lq < Lk (reading: the queries are the last Lq positions of the keys, so key j
+    is visible to row i iff j <= i + Lk - Lq): scalar loops with exact summation; torch's
+    float64 scaled_dot_product_attention with that boolean mask; row i equals non-causal
+    attention over the key prefix 0..i+Lk-Lq; the last row sees every key."""
+    import torch
+
+    for seed, (Lq, Lk, D) in enumerate([(1, 5, 2), (3, 7, 4), (6, 6, 3), (2, 9, 8)]):
+        q, k, v = _qkv(400 + seed, 1, 1, Lq, Lk, D)
+        scale = 0.41 + 0.1 * seed
+        O, LSE = attn(q, k, v, scale, True)
+        for i in range(Lq):
+            js = range(0, i + Lk - Lq + 1)
+            s_ = [scale * math.fsum(q[0, 0, i, d] * k[0, 0, j, d] for d in range(D)) for j in js]
+            mx = max(s_)
+            w = [math.exp(x - mx) for x in s_]
+            tot = math.fsum(w)
+            for d in range(D):
+                ref = math.fsum(w[t] * v[0, 0, j, d] for t, j in enumerate(js)) / tot
+                assert abs(O[0, 0, i, d] - ref) <= 1e-13 * (1 + abs(ref)), (Lq, Lk, i, d)
+            assert abs(LSE[0, 0, i] - (mx + math.log(tot))) <= 1e-13 * (1 + abs(mx)), (Lq, Lk, i)
+    q, k, v = _qkv(410, 2, 2, 11, 30, 8)
+    scale = 0.3
+    O, LSE = attn(q, k, v, scale, True)
+    mask = torch.arange(30)[None, :] <= torch.arange(11)[:, None] + 19
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+    S = ((tq @ tk.transpose(-1, -2)) * scale).masked_fill(~mask, float("-inf"))
+    np.testing.assert_allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(LSE, torch.logsumexp(S, dim=-1).numpy(), rtol=0, atol=1e-12)
+    for i in (0, 5, 10):
+        Oi, Li = attn(q[:, :, i : i + 1], k[:, :, : i + 20], v[:, :, : i + 20], scale, False)
+        np.testing.assert_allclose(O[:, :, i], Oi[:, :, 0], atol=1e-13)
+        np.testing.assert_allclose(LSE[:, :, i], Li[:, :, 0], atol=1e-13)
+
+
 PINS = [pin_golden, pin_brute_force, pin_probabilities, pin_zero_queries, pin_constant_values,
-        pin_one_large_logit, pin_sdpa, pin_invariances, pin_causal_prefix, pin_scale_homogeneity]
+        pin_one_large_logit, pin_sdpa, pin_invariances, pin_causal_prefix, pin_scale_homogeneity,
+        pin_causal_bottom_right]
 
 
 def _oracle_attn(q, k, v, scale, causal):
@@ -278,9 +315,11 @@ def test_pin_holds_for_oracle(pin):
 MUTANTS = {
     "dropped_scale": ("S = (q[r] @ kT) * scale", "S = (q[r] @ kT)"),
     "negated_scale": ("S = (q[r] @ kT) * scale", "S = (q[r] @ kT) * -scale"),
-    "mask_excludes_diagonal": ("> r[:, None]] = -np.inf", ">= r[:, None]] = -np.inf"),
-    "mask_one_extra_key": ("> r[:, None]] = -np.inf", "> r[:, None] + 1] = -np.inf"),
-    "mask_transposed": ("> r[:, None]] = -np.inf", "< r[:, None]] = -np.inf"),
+    "mask_excludes_diagonal": ("> r[:, None] + off] = -np.inf", ">= r[:, None] + off] = -np.inf"),
+    "mask_one_extra_key": ("> r[:, None] + off] = -np.inf", "> r[:, None] + off + 1] = -np.inf"),
+    "mask_transposed": ("> r[:, None] + off] = -np.inf", "< r[:, None] + off] = -np.inf"),
+    "mask_top_left": ("> r[:, None] + off] = -np.inf", "> r[:, None]] = -np.inf"),
+    "mask_offset_reversed": ("> r[:, None] + off] = -np.inf", "> r[:, None] - off] = -np.inf"),
     "no_max_in_lse": ("LSE[c0 : c0 + chunk] = m + np.log(l)", "LSE[c0 : c0 + chunk] = np.log(l)"),
     "lse_base2": ("m + np.log(l)", "m + np.log2(l)"),
     "no_normalisation": ("(P @ v) / l[:, None]", "(P @ v)"),
@@ -361,7 +400,7 @@ def test_rows_subset_matches_full():
     np.testing.assert_allclose(Ls, LSE[:, :, rows], rtol=0, atol=1e-14)
 
 
-def test_causal_requires_square():
-    q, k, v = _qkv(4, 1, 1, 4, 6, 2)
+def test_causal_with_more_queries_than_keys_is_rejected():
+    q, k, v = _qkv(420, 1, 1, 6, 4, 2)
     with pytest.raises(ValueError):
-        attention_fp64(q, k, v, 1.0, True)
+        attention_fp64(q, k, v, 0.5, True)
