@@ -21,8 +21,9 @@
  * its key tiles are seen ([DF §2.2], first and second layers; [OP §1], fusion
  * and tiling).  The per-row log-sum-exp is the softmax statistic kept for a
  * backward pass ([DF §2.2], third layer; [AI §3.2] sizes it as one float per
- * row).  With causal != 0, key j is visible to row i iff j <= i ([DF §4.1],
- * causal flag; diagonal included).
+ * row).  With causal != 0, key j is visible to row i iff j <= i + (Lk - Lq)
+ * ([DF §4.1], causal flag; diagonal included; for Lq < Lk the queries are taken
+ * as the last Lq positions of the keys, "bottom-right" alignment).
  *
  * Precision: q, k, v and o are fp16 or bf16; products are accumulated in fp32;
  * the softmax runs in fp32 ([OP §4.1]: half-precision inputs, fp32 softmax
@@ -33,6 +34,7 @@
 #ifndef FA355_H
 #define FA355_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -56,10 +58,12 @@ typedef enum {
   FA_ERR_DTYPE = -4,        /* dtype is not FA_DTYPE_F16 or FA_DTYPE_BF16                        */
   FA_ERR_ALIGN = -5,        /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned        */
   FA_ERR_SCALE = -6,        /* scale is NaN or infinite                                          */
-  FA_ERR_CAUSAL_SHAPE = -7, /* causal with Lq != Lk (the alignment of such a mask is undefined)  */
+  FA_ERR_CAUSAL_SHAPE = -7, /* causal with Lq > Lk (rows would have no visible key)              */
   FA_ERR_DEVICE = -8,       /* the current device has no gfx950 code object for the kernel       */
   FA_ERR_LAUNCH = -9,       /* the kernel launch failed (HIP code in fa_last_hip_error())        */
-  FA_ERR_STRIDE = -10       /* fa_fwd_strided: a stride < 0, or a row stride < D                 */
+  FA_ERR_STRIDE = -10,      /* fa_fwd_strided: a stride < 0, or a row stride < D                 */
+  FA_ERR_SPLITS = -11,      /* fa_fwd_splitkv: num_splits outside 1..64                          */
+  FA_ERR_WORKSPACE = -12    /* fa_fwd_splitkv: workspace smaller than the size query returns     */
 } fa_status;
 
 /*
@@ -76,7 +80,7 @@ typedef enum {
  *   scale               logit multiplier, any finite value (typically 1/sqrt(D));
  *                       applied in fp32 to the fp32 dot products.
  *   causal              0: every key is visible; non-zero: key j visible to row i iff
- *                       j <= i, which requires Lq == Lk.
+ *                       j <= i + (Lk - Lq), which requires Lq <= Lk.
  *   dtype               FA_DTYPE_F16 or FA_DTYPE_BF16 (q, k, v and o share it).
  *   stream              HIP stream to enqueue on.
  *
@@ -120,6 +124,34 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
                    int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
                    const int64_t* o_stride, float scale, int causal, int dtype, fa_stream_t stream);
+
+/*
+ * fa_fwd_splitkv — fa_fwd_strided with the keys of every (batch, head, query
+ * tile) divided into num_splits equal ranges computed by separate workgroups,
+ * then merged: each range yields its unnormalised output and the running max
+ * and exp-sums of its rows, and a second kernel combines them exactly (the
+ * streaming update of [DF §2.2] applied across ranges), so the result equals
+ * one pass up to fp32 rounding.  This fills the GPU when B*H*ceil(Lq/256) is
+ * small; it is also the merge a multi-GPU split of the keys would use.
+ *
+ *   num_splits        1..64 (FA_ERR_SPLITS otherwise); 1 is fa_fwd_strided and
+ *                     ignores the workspace.
+ *   workspace         device memory of at least
+ *                     fa_fwd_splitkv_workspace_size(B, H, Lq, D, num_splits)
+ *                     bytes (FA_ERR_WORKSPACE), 256-byte aligned (FA_ERR_ALIGN),
+ *                     owned by the caller, overwritten by the call, free again
+ *                     once the stream has passed it; NULL is FA_ERR_NULL when
+ *                     num_splits > 1.  (Lq + 256)*D*4 must stay below 2^32.
+ *
+ * Two kernels are enqueued on stream (partials, then merge).  Calls that share
+ * one workspace must be ordered on one stream.
+ */
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Lq, int D, int num_splits);
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+                   int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                   const int64_t* o_stride, float scale, int causal, int dtype, int num_splits, void* workspace,
+                   size_t workspace_bytes, fa_stream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -48,8 +48,8 @@ def call_strided(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, Lq=64, Lk=6
 
 
 def test_header_declares_the_abi():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_status_string", "fa_last_hip_error",
-                                    "fa_version"]
+    assert declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
+                                    "fa_status_string", "fa_last_hip_error", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -64,8 +64,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert fa.fa_version() == 10100
-    for code in range(0, -11, -1):
+    assert fa.fa_version() == 10200
+    for code in range(0, -13, -1):
         s = fa.fa_status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in fa.fa_status_string(5)
@@ -118,8 +118,10 @@ def test_scale(scale):
     assert call(scale=scale) == -6
 
 
-def test_causal_requires_square():
-    assert call(causal=1, Lq=64, Lk=65) == -7
+def test_causal_requires_no_more_queries_than_keys():
+    # Lq <= Lk is accepted (bottom-right alignment); make a later check fail so nothing launches
+    assert call(causal=1, Lq=64, Lk=65, D=96) == -3
+    assert call(causal=1, Lq=65, Lk=64) == -7
     assert call(causal=7, Lq=3, Lk=2) == -7
 
 
@@ -152,7 +154,7 @@ def test_strided_valid_strides_reach_later_checks():
     # broadcast K/V (batch and head stride 0) and padded rows are accepted; a later
     # check (head dim) fails, so nothing launches
     assert call_strided(strides={"k": (0, 0, 136), "v": (0, 0, 256)}, D=96) == -3
-    assert call_strided(causal=1, Lq=64, Lk=65) == -7
+    assert call_strided(causal=1, Lq=65, Lk=64) == -7
     assert call_strided(scale=float("nan")) == -6
 
 
@@ -204,3 +206,52 @@ def test_product_path_does_not_touch_the_oracle():
                     text = f.read()
                 assert "oracle" not in text.lower(), name
                 assert "scaled_dot_product_attention" not in text, name
+
+
+def call_split(splits=2, ws=P[4] * 16, ws_bytes=None, B=1, H=2, Lq=300, Lk=500, D=128, **kw):
+    if ws_bytes is None:
+        ws_bytes = fa.fa_fwd_splitkv_workspace_size(B, H, Lq, D, splits)
+    st = {"q": (H * Lq * D, Lq * D, D), "k": (H * Lk * D, Lk * D, D), "v": (H * Lk * D, Lk * D, D),
+          "o": (H * Lq * D, Lq * D, D)}
+    arr = [(ctypes.c_int64 * 3)(*st[n]) for n in ("q", "k", "v", "o")]
+    ptr = [ctypes.cast(a, ctypes.c_void_p) for a in arr]
+    args = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], scale=0.125, causal=0, dtype=1)
+    args.update(kw)
+    return fa.lib.fa_fwd_splitkv(args["q"], args["k"], args["v"], args["o"], args["lse"], B, H, Lq, Lk, D, *ptr,
+                                 args["scale"], args["causal"], args["dtype"], splits, ws, ws_bytes, None)
+
+
+def test_splitkv_workspace_size():
+    # partial outputs (fp32 [splits, B*H, Lq, D]) then row statistics (fp32 [splits, B*H, Lq, 4])
+    assert fa.fa_fwd_splitkv_workspace_size(2, 3, 100, 128, 4) == 4 * 6 * 100 * (128 + 4) * 4
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 7, 64, 3) == 3 * 7 * (64 + 4) * 4
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 7, 64, 1) == 0
+    for bad in [(0, 1, 7, 64, 2), (1, 1, 7, 96, 2), (1, 1, 7, 64, 0), (1, 1, 7, 64, 65), (1, 0, 7, 64, 2)]:
+        assert fa.fa_fwd_splitkv_workspace_size(*bad) == 0
+
+
+@pytest.mark.parametrize("splits", [0, -1, 65, 1000])
+def test_splitkv_split_count(splits):
+    assert call_split(splits=splits, ws_bytes=1 << 40) == -11
+
+
+def test_splitkv_workspace_errors():
+    assert call_split(ws=None) == -1                         # no workspace
+    assert call_split(ws=P[4] * 16 + 16) == -5                # not 256-byte aligned
+    need = fa.fa_fwd_splitkv_workspace_size(1, 2, 300, 128, 2)
+    assert call_split(ws_bytes=need - 1) == -12               # too small
+    # enough workspace: a later check fails so nothing launches
+    assert call_split(ws_bytes=need, scale=float("nan")) == -6
+    assert call_split(ws_bytes=need, causal=1, Lq=501, Lk=500) == -7
+
+
+def test_splitkv_partial_slab_limit():
+    # (Lq + 256) * D * 4 must stay below 2^32 for the fp32 partials
+    assert call_split(Lq=8_388_352, Lk=8_388_352, ws_bytes=1 << 62) == -2
+
+
+def test_suggest_num_splits():
+    assert fa.suggest_num_splits(4, 32, 4096, 4096, 128, True) == 1        # 2,048 workgroups fill 256 CUs
+    assert fa.suggest_num_splits(1, 32, 2048, 2048, 128, True) == 2        # 256 workgroups, causal
+    assert fa.suggest_num_splits(1, 1, 128, 128, 64, False) == 1           # too few keys to split
+    assert 1 <= fa.suggest_num_splits(1, 2, 256, 65536, 128, False) <= 64

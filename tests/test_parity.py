@@ -327,3 +327,75 @@ def test_strided_train_shape_sampled():
     oc, lc = o.cpu(), lse.cpu()
     for b, h in heads:
         compare(oc[b, h][rows], lc[b, h][rows], O_ref[b, h], L_ref[b, h], w.dtype, f"strided train ({b},{h})")
+
+
+# ------------------------------------------------------------------------------------------
+# causal with Lq < Lk (bottom-right alignment) and key splits (fa_fwd_splitkv)
+# ------------------------------------------------------------------------------------------
+
+BR_CASES = [(1, 2, 1, 1000, 128, "bf16"), (1, 2, 100, 1000, 64, "fp16"), (2, 3, 300, 301, 128, "bf16"),
+            (1, 1, 257, 4000, 128, "fp16"), (1, 2, 64, 64, 64, "bf16"), (1, 2, 700, 777, 64, "bf16")]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype", BR_CASES,
+                         ids=[f"B{b}H{h}_{lq}x{lk}_D{d}_{dt}" for b, h, lq, lk, d, dt in BR_CASES])
+def test_causal_bottom_right(B, H, Lq, Lk, D, dtype):
+    inp = ai.make_custom(B, H, Lq, Lk, D, dtype, True, seed=30_000 + 7 * Lq + Lk + D)
+    note(f"causal bottom-right B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype}")
+    o, lse = run_gpu(inp)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], True)
+    compare(o, lse, O_ref, L_ref, dtype, "bottom-right")
+
+
+SPLIT_CASES = [(1, 2, 300, 300, 128, "bf16", True, 2), (1, 2, 300, 300, 128, "bf16", True, 8),
+               (2, 2, 200, 1000, 64, "fp16", False, 3), (1, 2, 100, 2000, 128, "fp16", True, 5),
+               (1, 1, 1, 4096, 128, "bf16", False, 16), (1, 3, 513, 513, 64, "bf16", True, 4),
+               (1, 2, 130, 65, 128, "fp16", False, 64)]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal,splits", SPLIT_CASES,
+                         ids=[f"B{b}H{h}_{lq}x{lk}_D{d}_{dt}_{'c' if c else 'nc'}_s{s}"
+                              for b, h, lq, lk, d, dt, c, s in SPLIT_CASES])
+def test_splitkv(B, H, Lq, Lk, D, dtype, causal, splits):
+    inp = ai.make_custom(B, H, Lq, Lk, D, dtype, causal, seed=40_000 + Lq + Lk + splits)
+    note(f"split-KV B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype} causal={causal} splits={splits}")
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=inp["scale"], num_splits=splits)
+    torch.cuda.synchronize()
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], causal)
+    compare(o, lse, O_ref, L_ref, dtype, f"split-KV x{splits}")
+    # the merge reproduces one pass up to fp32 rounding of the combination
+    o1, l1 = run_gpu(inp)
+    assert (lse.cpu() - l1.cpu()).abs().max().item() <= 1e-4
+    assert (o.cpu().double() - o1.cpu().double()).abs().max().item() <= 2 * TOL[dtype]
+
+
+def test_splitkv_workspace_reuse_and_views():
+    # one workspace for two calls in a row (the second smaller), on [B, L, H, D] views
+    big = ai.make_custom(2, 4, 600, 600, 128, "bf16", True, seed=41_001)
+    small = ai.make_custom(1, 2, 300, 500, 128, "bf16", True, seed=41_002)
+    ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(2, 4, 600, 128, 4), dtype=torch.uint8, device=DEV)
+    outs = []
+    for inp in (big, small):
+        q, k, v, o, _ = _views("blhd", inp)
+        outs.append(fa.fa_fwd_splitkv(q, k, v, o, causal=True, scale=inp["scale"], num_splits=4, workspace=ws))
+    torch.cuda.synchronize()
+    for inp, (o, lse) in zip((big, small), outs):
+        O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], True)
+        compare(o.cpu().contiguous(), lse, O_ref, L_ref, "bf16", "split-KV reuse")
+
+
+def test_splitkv_llama_shape_sampled():
+    w = ai.WORKLOADS["llama7b_2k"]
+    inp = ai.make_inputs(w)
+    splits = fa.suggest_num_splits(w.B, w.H, w.Lq, w.Lk, w.D, w.causal)
+    note(f"split-KV llama7b_2k with {splits} splits")
+    assert splits > 1
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd(q, k, v, causal=True, scale=w.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    heads, rows = _sample(w, seed=5)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, True, rows=rows, heads=heads)
+    oc, lc = o.cpu(), lse.cpu()
+    for b, h in heads:
+        compare(oc[b, h][rows], lc[b, h][rows], O_ref[b, h], L_ref[b, h], w.dtype, f"llama split ({b},{h})")

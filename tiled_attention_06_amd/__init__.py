@@ -5,9 +5,10 @@ kernel behind the C ABI declared in ``include/fa355.h``.  PyTorch supplies
 device memory and the current stream.  There is no fallback: if the compiled
 library is missing, importing this package raises ImportError.
 
-Names follow the C ABI: ``fa_fwd``, ``fa_fwd_strided``, ``fa_status_string``,
-``fa_last_hip_error``, ``fa_version``; ``fa_fwd_qkvpacked`` is a view helper over
-``fa_fwd_strided`` for a packed [B, L, 3, H, D] qkv buffer.
+Names follow the C ABI: ``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_splitkv``,
+``fa_fwd_splitkv_workspace_size``, ``fa_status_string``, ``fa_last_hip_error``,
+``fa_version``; ``fa_fwd_qkvpacked`` is a view helper over ``fa_fwd_strided`` for
+a packed [B, L, 3, H, D] qkv buffer, and ``suggest_num_splits`` a host heuristic.
 """
 
 from __future__ import annotations
@@ -18,7 +19,8 @@ import os
 
 import torch
 
-__all__ = ["fa_fwd", "fa_fwd_strided", "fa_fwd_qkvpacked", "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH",
+__all__ = ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_qkvpacked",
+           "suggest_num_splits", "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH",
            "FA_DTYPE_F16", "FA_DTYPE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
@@ -39,6 +41,11 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, ctypes.c_float, i, i, vp]
     lib.fa_fwd_strided.restype = i
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, ctypes.c_float, i, i, i, vp,
+                                   ctypes.c_size_t, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -95,12 +102,22 @@ def _check(q, k, v, o, lse):
     return B, H, Lq, Lk, D, o, lse
 
 
-def _launch(strided, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream):
+def _launch(strided, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream, splits=1, workspace=None):
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    if not strided:
+    if splits != 1:
+        need = fa_fwd_splitkv_workspace_size(B, H, Lq, D, splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        st = [(ctypes.c_int64 * 3)(*t.stride()[:3]) for t in (q, k, v, o)]
+        code = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, H, Lq, Lk, D, *[ctypes.cast(s_, ctypes.c_void_p) for s_ in st],
+                                  float(scale), 1 if causal else 0, _DTYPES[q.dtype], int(splits),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  stream.cuda_stream)
+    elif not strided:
         code = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                           B, H, Lq, Lk, D, float(scale), 1 if causal else 0, _DTYPES[q.dtype], stream.cuda_stream)
     else:
@@ -115,19 +132,21 @@ def _launch(strided, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream):
 
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
            lse: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
-           stream: torch.cuda.Stream | None = None):
+           stream: torch.cuda.Stream | None = None, num_splits: int = 1):
     """Enqueue the attention forward pass on ``stream`` (default: torch's current stream of q's device).
 
     q: [B, H, Lq, D]; k, v: [B, H, Lk, D]; fp16/bf16 tensors on one GPU, dense or
     any strided views with a contiguous head dim (a [B, L, H, D] tensor passed as
     ``x.transpose(1, 2)`` is used in place).  o (q's shape and dtype, dense or a
     view) and lse ([B, H, Lq], float32, dense) are allocated when not given.
-    ``scale`` defaults to 1/sqrt(D).  Dense inputs go through the C ``fa_fwd``,
-    others through ``fa_fwd_strided``.  Returns (o, lse).
+    ``scale`` defaults to 1/sqrt(D).  Causal with Lq < Lk aligns the queries with
+    the last Lq keys.  Dense inputs go through the C ``fa_fwd``, others through
+    ``fa_fwd_strided``; ``num_splits`` > 1 goes through ``fa_fwd_splitkv`` with a
+    workspace allocated here (see ``suggest_num_splits``).  Returns (o, lse).
     """
     B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
     dense = all(t.is_contiguous() for t in (q, k, v, o))
-    return _launch(not dense, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream)
+    return _launch(not dense, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream, num_splits)
 
 
 def fa_fwd_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
@@ -136,6 +155,39 @@ def fa_fwd_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
     """Like ``fa_fwd``, always through the C ``fa_fwd_strided`` (the tensors' own strides)."""
     B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
     return _launch(True, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream)
+
+
+def fa_fwd_splitkv_workspace_size(B: int, H: int, Lq: int, D: int, num_splits: int) -> int:
+    """Bytes of workspace ``fa_fwd_splitkv`` needs (0 for num_splits == 1 or invalid arguments)."""
+    return int(lib.fa_fwd_splitkv_workspace_size(B, H, Lq, D, num_splits))
+
+
+def fa_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
+                   num_splits: int = 2, workspace: torch.Tensor | None = None,
+                   stream: torch.cuda.Stream | None = None):
+    """Like ``fa_fwd`` through the C ``fa_fwd_splitkv``: the keys of each query tile are divided into
+    ``num_splits`` ranges and merged exactly.  ``workspace`` (a device tensor of at least
+    ``fa_fwd_splitkv_workspace_size`` bytes) is allocated when not given."""
+    B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
+    if num_splits == 1:
+        return _launch(True, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream)
+    return _launch(True, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream, num_splits, workspace)
+
+
+def suggest_num_splits(B: int, H: int, Lq: int, Lk: int, D: int, causal: bool, num_cu: int = 256) -> int:
+    """Key splits that give about two workgroups per CU, with at least four 64-key tiles per split.
+
+    One workgroup covers 256 query rows; with fewer workgroups than twice the CUs (and, causal,
+    an uneven amount of work per workgroup) splitting the keys fills the GPU.
+    """
+    wgs = B * H * ((Lq + 255) // 256)
+    if wgs >= 2 * num_cu:
+        return 1
+    tiles = (Lk + 63) // 64
+    if causal:
+        tiles = max(1, tiles // 2)  # the average query tile sees about half of the keys
+    return int(max(1, min(64, -(-2 * num_cu // wgs), tiles // 4)))
 
 
 def fa_fwd_qkvpacked(qkv: torch.Tensor, o: torch.Tensor | None = None, lse: torch.Tensor | None = None, *,

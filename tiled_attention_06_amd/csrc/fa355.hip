@@ -3,8 +3,9 @@
 // Argument validation happens here, on the host, before any HIP call, so every
 // FA_ERR_* of a bad argument can be produced without a GPU.  A valid call
 // selects the kernel instance for (head dim, dtype, causal) and enqueues one
-// launch on the caller's stream.  No allocation, no synchronisation, no global
-// mutable state apart from the per-thread last HIP error.
+// launch on the caller's stream (two with key splits: partials, then the merge).
+// No allocation, no synchronisation, no global mutable state apart from the
+// per-thread last HIP error.
 
 #include <math.h>
 #include <stdint.h>
@@ -18,12 +19,10 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
+constexpr int kMaxSplits = 64;
 
-template <int D, int DT, bool CAUSAL>
-int launch(const fa355::FwdParams& p, hipStream_t stream) {
-  using G = fa355::Geo<D>;
-  hipLaunchKernelGGL((fa355::fa_fwd_kernel<D, DT, CAUSAL>), dim3(p.num_wg), dim3(G::NT), 0, stream, p);
+int launch_status() {
   const hipError_t e = hipGetLastError();
   if (e == hipSuccess) return FA_OK;
   g_last_hip_error = (int)e;
@@ -33,22 +32,37 @@ int launch(const fa355::FwdParams& p, hipStream_t stream) {
   return FA_ERR_LAUNCH;
 }
 
+template <int D, int DT, bool CAUSAL>
+int launch(const fa355::FwdParams& p, const fa355::MergeParams& m, hipStream_t stream) {
+  using G = fa355::Geo<D>;
+  hipLaunchKernelGGL((fa355::fa_fwd_kernel<D, DT, CAUSAL>), dim3(p.num_wg), dim3(G::NT), 0, stream, p);
+  int st = launch_status();
+  if (st != FA_OK || p.n_split == 1) return st;
+  constexpr int rows_per_block = 256 / (D / 4);
+  const int64_t rows = (int64_t)m.bh * m.Lq;
+  hipLaunchKernelGGL((fa355::fa_merge_kernel<D, DT>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+                     dim3(256), 0, stream, m);
+  return launch_status();
+}
+
 template <int D>
-int dispatch_dtype(const fa355::FwdParams& p, int dtype, bool causal, hipStream_t s) {
+int dispatch_dtype(const fa355::FwdParams& p, const fa355::MergeParams& m, int dtype, bool causal, hipStream_t s) {
   if (dtype == FA_DTYPE_BF16)
-    return causal ? launch<D, fa355::DT_BF16, true>(p, s) : launch<D, fa355::DT_BF16, false>(p, s);
-  return causal ? launch<D, fa355::DT_F16, true>(p, s) : launch<D, fa355::DT_F16, false>(p, s);
+    return causal ? launch<D, fa355::DT_BF16, true>(p, m, s) : launch<D, fa355::DT_BF16, false>(p, m, s);
+  return causal ? launch<D, fa355::DT_F16, true>(p, m, s) : launch<D, fa355::DT_F16, false>(p, m, s);
 }
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
-}  // namespace
+// bytes of the partials workspace: outputs, then row statistics
+size_t ws_o_bytes(int B, int H, int Lq, int D, int splits) { return (size_t)splits * B * H * Lq * D * 4; }
+size_t ws_bytes(int B, int H, int Lq, int D, int splits) {
+  return splits <= 1 ? 0 : ws_o_bytes(B, H, Lq, D, splits) + (size_t)splits * B * H * Lq * 4 * 4;
+}
 
-extern "C" {
-
-int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
-                   int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
-                   const int64_t* o_stride, float scale, int causal, int dtype, fa_stream_t stream) {
+int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk, int D,
+        const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride, const int64_t* o_stride,
+        float scale, int causal, int dtype, int splits, void* ws, size_t ws_size, fa_stream_t stream) {
   if (!q || !k || !v || !o || !lse || !q_stride || !k_stride || !v_stride || !o_stride) return FA_ERR_NULL;
   if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
@@ -61,16 +75,23 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
   for (int i = 0; i < 4; ++i)  // every row starts on a 16-byte boundary
     if (st[i][0] % 8 || st[i][1] % 8 || st[i][2] % 8) return FA_ERR_ALIGN;
   if (!isfinite(scale)) return FA_ERR_SCALE;
-  if (causal && Lq != Lk) return FA_ERR_CAUSAL_SHAPE;
+  if (causal && Lq > Lk) return FA_ERR_CAUSAL_SHAPE;
+  if (splits < 1 || splits > kMaxSplits) return FA_ERR_SPLITS;
+  if (splits > 1) {
+    if (!ws) return FA_ERR_NULL;
+    if (!aligned(ws, 256)) return FA_ERR_ALIGN;
+    if (ws_size < ws_bytes(B, H, Lq, D, splits)) return FA_ERR_WORKSPACE;
+  }
 
   // One head's slab is addressed with 32-bit byte offsets, including up to 256
   // rows of tile padding past its end; batch and head offsets are 64-bit.
   const int64_t lens[4] = {Lq, Lk, Lk, Lq};
   for (int i = 0; i < 4; ++i)
     if (((lens[i] + 256) * st[i][2] + D) * 2 >= (1ll << 32)) return FA_ERR_SHAPE;
+  if (splits > 1 && ((int64_t)Lq + 256) * D * 4 >= (1ll << 32)) return FA_ERR_SHAPE;  // one partial slab
   const int BR = D == 128 ? fa355::Geo<128>::BR : fa355::Geo<64>::BR;
   const int64_t n_qt = ((int64_t)Lq + BR - 1) / BR;
-  const int64_t num_wg = (int64_t)B * H * n_qt;
+  const int64_t num_wg = (int64_t)B * H * n_qt * splits;
   if ((int64_t)B * H >= (1ll << 31) || num_wg >= (1ll << 22)) return FA_ERR_SHAPE;
 
   fa355::FwdParams p;
@@ -86,9 +107,13 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
   p.k_sb = k_stride[0], p.k_sh = k_stride[1], p.k_sl = (int)k_stride[2];
   p.v_sb = v_stride[0], p.v_sh = v_stride[1], p.v_sl = (int)v_stride[2];
   p.o_sb = o_stride[0], p.o_sh = o_stride[1], p.o_sl = (int)o_stride[2];
+  p.kv_off = Lk - Lq;  // used only when causal (then >= 0)
   p.n_qt = (int)n_qt;
+  p.n_split = splits;
   p.num_wg = (int)num_wg;
   p.bh = (int)((int64_t)B * H);
+  p.ws_o = splits > 1 ? (float*)ws : nullptr;
+  p.ws_ml = splits > 1 ? (float*)((char*)ws + ws_o_bytes(B, H, Lq, D, splits)) : nullptr;
   p.xcd_remap = (num_wg % 8 == 0) ? 1 : 0;
   // The softmax runs in base 2 with the scale folded into one positive factor;
   // a negative scale negates Q (exact in fp16/bf16) and a zero scale zeroes it.
@@ -97,8 +122,30 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
   p.q_and = scale == 0.0f ? 0u : 0xffffffffu;
   p.q_xor = scale < 0.0f ? 0x80008000u : 0u;
 
+  fa355::MergeParams m;
+  m.ws_o = p.ws_o;
+  m.ws_ml = p.ws_ml;
+  m.o = o;
+  m.lse = lse;
+  m.Lq = Lq;
+  m.H = H;
+  m.n_split = splits;
+  m.bh = p.bh;
+  m.o_sb = p.o_sb, m.o_sh = p.o_sh, m.o_sl = p.o_sl;
+
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return D == 128 ? dispatch_dtype<128>(p, dtype, causal != 0, s) : dispatch_dtype<64>(p, dtype, causal != 0, s);
+  return D == 128 ? dispatch_dtype<128>(p, m, dtype, causal != 0, s) : dispatch_dtype<64>(p, m, dtype, causal != 0, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+                   int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                   const int64_t* o_stride, float scale, int causal, int dtype, fa_stream_t stream) {
+  return fwd(q, k, v, o, lse, B, H, Lq, Lk, D, q_stride, k_stride, v_stride, o_stride, scale, causal, dtype, 1,
+             nullptr, 0, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk, int D,
@@ -106,7 +153,20 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   // dense [B, H, L, D]: the strided form with the natural strides
   const int64_t sq[3] = {(int64_t)H * Lq * D, (int64_t)Lq * D, D};
   const int64_t sk[3] = {(int64_t)H * Lk * D, (int64_t)Lk * D, D};
-  return fa_fwd_strided(q, k, v, o, lse, B, H, Lq, Lk, D, sq, sk, sk, sq, scale, causal, dtype, stream);
+  return fwd(q, k, v, o, lse, B, H, Lq, Lk, D, sq, sk, sk, sq, scale, causal, dtype, 1, nullptr, 0, stream);
+}
+
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Lq, int D, int num_splits) {
+  if (B < 1 || H < 1 || Lq < 1 || (D != 64 && D != 128) || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  return ws_bytes(B, H, Lq, D, num_splits);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+                   int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                   const int64_t* o_stride, float scale, int causal, int dtype, int num_splits, void* workspace,
+                   size_t workspace_bytes, fa_stream_t stream) {
+  return fwd(q, k, v, o, lse, B, H, Lq, Lk, D, q_stride, k_stride, v_stride, o_stride, scale, causal, dtype,
+             num_splits, workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {
@@ -118,10 +178,12 @@ const char* fa_status_string(int status) {
     case FA_ERR_DTYPE: return "fa_fwd: dtype must be FA_DTYPE_F16 (0) or FA_DTYPE_BF16 (1)";
     case FA_ERR_ALIGN: return "fa_fwd: q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_SCALE: return "fa_fwd: scale must be finite";
-    case FA_ERR_CAUSAL_SHAPE: return "fa_fwd: causal attention requires Lq == Lk";
+    case FA_ERR_CAUSAL_SHAPE: return "fa_fwd: causal attention requires Lq <= Lk";
     case FA_ERR_DEVICE: return "fa_fwd: no gfx950 kernel for the current device";
     case FA_ERR_LAUNCH: return "fa_fwd: kernel launch failed (see fa_last_hip_error)";
     case FA_ERR_STRIDE: return "fa_fwd: strides must be >= 0, with a row stride of at least D";
+    case FA_ERR_SPLITS: return "fa_fwd_splitkv: num_splits must be between 1 and 64";
+    case FA_ERR_WORKSPACE: return "fa_fwd_splitkv: workspace smaller than fa_fwd_splitkv_workspace_size()";
     default: return "fa_fwd: unknown status code";
   }
 }

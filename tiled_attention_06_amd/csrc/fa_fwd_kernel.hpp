@@ -64,6 +64,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -93,9 +94,13 @@ struct FwdParams {
   // element strides of batch, head and row; the head dim is contiguous
   int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
   int q_sl, k_sl, v_sl, o_sl;
+  int kv_off;       // causal: key position of query row 0 (Lk - Lq >= 0)
   int n_qt;         // query tiles per head: ceil(Lq / BR)
-  int num_wg;       // B * H * n_qt
+  int n_split;      // key splits per (batch*head, query tile); 1: one pass, output written directly
+  int num_wg;       // B * H * n_qt * n_split
   int bh;           // B * H
+  float* ws_o;      // n_split > 1: unnormalised partial outputs, fp32 [n_split][B*H][Lq][D]
+  float* ws_ml;     // n_split > 1: per row (m, l_f, l_r, 0), fp32 [n_split][B*H][Lq][4]
   int xcd_remap;    // 1: group consecutive work items on one XCD
   float c;          // |scale| * log2(e), or log2(e) when scale == 0 (always > 0)
   uint32_t q_and;   // 0xffffffff, or 0 when scale == 0 (Q forced to zero)
@@ -143,6 +148,10 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
 // One 16-byte-per-lane HBM -> LDS copy (buffer_load_dwordx4 ... lds): lane l's
@@ -270,7 +279,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // consecutive items (all query tiles of one head) on one XCD, whose L2 then
   // serves the K/V re-reads of that head.
   const int bid = blockIdx.x;
-  const int item = p.xcd_remap ? (bid & 7) * (p.num_wg >> 3) + (bid >> 3) : bid;
+  const int item_s = p.xcd_remap ? (bid & 7) * (p.num_wg >> 3) + (bid >> 3) : bid;
+  // the key splits of one (batch*head, query tile) are consecutive items
+  const int item = item_s / p.n_split, split = item_s - item * p.n_split;
   int bh, qt_r;
   if (CAUSAL) {
     // Heads in pairs, and within a pair the query tiles of both heads heaviest
@@ -341,12 +352,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // ---- key range of this workgroup
+  // Causal (bottom-right): query row i sits at key position i + off, key j is
+  // visible to it iff j <= i + off.
+  const int off = CAUSAL ? p.kv_off : 0;
   int n_kv = (Lk + BC - 1) / BC;
   if constexpr (CAUSAL) {
     const int last_row = min(i0 + G::BR, Lq) - 1;
-    n_kv = min(n_kv, last_row / BC + 1);
+    n_kv = min(n_kv, (last_row + off) / BC + 1);
   }
-  auto active = [&](int t) { return !CAUSAL || t * BC <= i0w + 31; };  // wave-uniform
+  // this item's tiles: [t_b, t_e), an equal share of the n_kv tiles per split
+  const int t_b = __builtin_amdgcn_readfirstlane((int)((int64_t)split * n_kv / p.n_split));
+  const int t_e = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * n_kv / p.n_split));
+  auto active = [&](int t) { return !CAUSAL || t * BC <= i0w + 31 + off; };  // wave-uniform
 
   // ---- Q tile -> VGPRs, as the B operand of Sᵀ = K·Qᵀ (column = query row l%32,
   // contraction slots of half g = head dims 16s+8g .. 16s+8g+7).  Rows past Lq read 0.
@@ -358,15 +375,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     qr[s] = (x & p.q_and) ^ p.q_xor;
   }
   // K and V tiles 0..NS-2, in the order the loop continues: K t, V t per tile.
-  copy_k(0, I0{});
-  copy_v(0, I0{});
-  if (n_kv > 1) {
-    copy_k(1, std::integral_constant<int, 1>{});
-    copy_v(1, std::integral_constant<int, 1>{});
+  // stage of tile t: (t - t_b) % NS
+  if (t_b < t_e) {
+    copy_k(t_b, I0{});
+    copy_v(t_b, I0{});
   }
-  if (n_kv > 2) {
-    copy_k(2, std::integral_constant<int, 2>{});
-    copy_v(2, std::integral_constant<int, 2>{});
+  if (t_b + 1 < t_e) {
+    copy_k(t_b + 1, std::integral_constant<int, 1>{});
+    copy_v(t_b + 1, std::integral_constant<int, 1>{});
+  }
+  if (t_b + 2 < t_e) {
+    copy_k(t_b + 2, std::integral_constant<int, 2>{});
+    copy_v(t_b + 2, std::integral_constant<int, 2>{});
   }
 
   // per-lane LDS offsets of the MFMA operand reads.  Tile row r sits in block
@@ -388,27 +408,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   const float c = p.c;
-  float m_run = NEG_INF, l_f = 0.f, l_r = 0.f;
+  // The running max starts at a finite -1e30 (not -inf): a row that sees no key of
+  // this item (possible only within a key split) keeps weights 2^(-inf) = 0 and
+  // sums 0, and the first visible tile always moves the max (scale 2^(-1e30) = 0).
+  float m_run = -1e30f, l_f = 0.f, l_r = 0.f;
   f32x16 oacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16{};
 
-  // Tiles [0, n_full) are visible in full to every row of the workgroup: no
-  // mask, every wave active.  Causal: tile t is full for row i0 iff 64t+63 <= i0.
+  // Tiles [t_b, n_full) are visible in full to every row of the workgroup: no
+  // mask, every wave active.  Causal: tile t is full for row i0 iff 64t+63 <= i0 + off.
   int n_full = Lk / BC;
-  if constexpr (CAUSAL) n_full = min(n_full, (i0 + 1) / BC);
+  if constexpr (CAUSAL) n_full = min(n_full, (i0 + off + 1) / BC);
+  n_full = min(n_full, t_e);
 
   // mask of a tile crossing the diagonal or the end of the keys (wave-uniform test)
   auto mask_tile = [&](f32x16(&S)[KB], int t) {
     const int j0 = t * BC;
-    const bool need_mask = (CAUSAL && j0 + BC - 1 > i0w) || (j0 + BC > Lk);
+    const bool need_mask = (CAUSAL && j0 + BC - 1 > i0w + off) || (j0 + BC > Lk);
     if (need_mask) {
       // key offset within the tile of S[kb][r] is 32kb + 8(r/4) + 4g + r%4
       // (lane-derived values taken afresh, see opaque())
       const int lane_m = opaque(tid) & 63;
       const int g_m = lane_m >> 5, row_m = i0w + (lane_m & 31);
       const int lim_tail = Lk - j0 - 4 * g_m;
-      const int lim = CAUSAL ? min(row_m - j0 - 4 * g_m + 1, lim_tail) : lim_tail;
+      const int lim = CAUSAL ? min(row_m + off - j0 - 4 * g_m + 1, lim_tail) : lim_tail;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -502,10 +526,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   auto kst_rt = [&](int st) -> unsigned char* { return st == 0 ? ks0 : st == 1 ? ks1 : st == 2 ? ks2 : ks3; };
   auto vst_rt = [&](int st) -> unsigned char* { return st == 0 ? vs0 : st == 1 ? vs1 : st == 2 ? vs2 : vs3; };
-  // K and V of tile t+NS-1, copied in iteration t into stage (t-1) % NS, which
-  // every wave finished with before the last barrier
+  // K and V of tile t+NS-1, copied in iteration t into the stage of tile t-1,
+  // which every wave finished with before the last barrier
   auto copies_rt = [&](int t) {
-    switch ((t + G::NS - 1) % G::NS) {
+    switch ((t - t_b + G::NS - 1) % G::NS) {
       case 0: copy_k(t + G::NS - 1, I0{}); copy_v(t + G::NS - 1, I0{}); break;
       case 1: copy_k(t + G::NS - 1, std::integral_constant<int, 1>{}); copy_v(t + G::NS - 1, std::integral_constant<int, 1>{}); break;
       case 2: copy_k(t + G::NS - 1, std::integral_constant<int, 2>{}); copy_v(t + G::NS - 1, std::integral_constant<int, 2>{}); break;
@@ -514,15 +538,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto end_iter = [&](int) { wait_join(); };
 
-  wait_join();  // tiles 0..2 and Q are in
+  wait_join();  // the first three tiles and Q are in
   f32x16 sA[KB], sB[KB];
   float mxA = NEG_INF, mxB = NEG_INF;
-  int t_tail = 0;
-  if (n_full > 0) {
+  int t_tail = t_b;
+  if (n_full > t_b) {
     // ---- full tiles, software-pipelined: iteration t computes Sᵀ of tile t+1
-    // (K stage (t+1) % NS) and its row max while the weights and PV of tile t (V
-    // stage t % NS) run; the rescale for tile t uses the max found one iteration
-    // earlier.  No mask and no branch inside the body.
+    // and its row max while the weights and PV of tile t run; the rescale for
+    // tile t uses the max found one iteration earlier.  No mask and no branch
+    // inside the body.
     compute_s(kst(I0{}), sA);
     mxA = row_max(sA);
     auto it_main = [&](int t, f32x16(&Sc)[KB], f32x16(&Sn)[KB], float& mxc, float& mxn, auto Pc) {
@@ -530,7 +554,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       using PN = std::integral_constant<int, (P + 1) % G::NS>;
       using PC = std::integral_constant<int, (P + G::NS - 1) % G::NS>;
       rescale(mxc);
-      if (t + G::NS - 1 < n_kv) {
+      if (t + G::NS - 1 < t_e) {
         copy_k(t + G::NS - 1, PC{});
         copy_v(t + G::NS - 1, PC{});
       }
@@ -542,7 +566,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       end_iter(t);
     };
     static_assert(G::NS == 4, "the loop below is unrolled over the stages");
-    for (int t = 0; t + 1 < n_full; t += 4) {
+    for (int t = t_b; t + 1 < n_full; t += 4) {
       it_main(t, sA, sB, mxA, mxB, I0{});
       if (t + 2 < n_full) it_main(t + 1, sB, sA, mxB, mxA, std::integral_constant<int, 1>{});
       if (t + 3 < n_full) it_main(t + 2, sA, sB, mxA, mxB, std::integral_constant<int, 2>{});
@@ -552,13 +576,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tf = n_full - 1;
     auto finish = [&](f32x16(&Sc)[KB], float mxc) {
       rescale(mxc);
-      if (tf + G::NS - 1 < n_kv) copies_rt(tf);
+      if (tf + G::NS - 1 < t_e) copies_rt(tf);
       u32x4 pb[KB][2];
       make_p(Sc, pb);
-      pv(pb, vst_rt(tf % G::NS));
+      pv(pb, vst_rt((tf - t_b) % G::NS));
       end_iter(tf);
     };
-    if (tf & 1)
+    if ((tf - t_b) & 1)
       finish(sB, mxB);
     else
       finish(sA, mxA);
@@ -566,10 +590,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   // ---- tiles that cross the diagonal or the end of the keys: not pipelined,
   // masked; a wave skips tiles above its own rows but still copies and joins.
-  for (int t = t_tail; t < n_kv; ++t) {
-    if (t + G::NS - 1 < n_kv) copies_rt(t);
+  for (int t = t_tail; t < t_e; ++t) {
+    if (t + G::NS - 1 < t_e) copies_rt(t);
     if (active(t)) {
-      compute_s(kst_rt(t % G::NS), sA);
+      compute_s(kst_rt((t - t_b) % G::NS), sA);
       // (scheduling barriers: the operand reads of one product are not hoisted
       // over the softmax, which would run this path out of registers)
       __builtin_amdgcn_sched_barrier(0);
@@ -579,17 +603,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       make_p(sA, pb);
       scale_o(any);
       __builtin_amdgcn_sched_barrier(0);
-      pv(pb, vst_rt(t % G::NS));
+      pv(pb, vst_rt((t - t_b) % G::NS));
     }
     end_iter(t);
   }
 
-  // ---- epilogue: normalise by the sum of the rounded weights, store O and LSE.
-  // The lane's row and half are derived afresh (see opaque()).
+  // ---- epilogue.  The lane's row and half are derived afresh (see opaque()).
   const int lane_e = opaque(tid) & 63;
   const int g_e = lane_e >> 5, row_e = i0w + (lane_e & 31);
   const float lf_t = xhalf_sum(l_f);
   const float lr_t = xhalf_sum(l_r);
+  if (p.n_split > 1) {
+    // A key split stores its partial result: the unnormalised output and the
+    // row's running max and two sums, all relative to that max (fa_merge_kernel
+    // combines the splits).  Rows >= Lq are dropped by the buffer range.
+    const size_t part = (size_t)split * p.bh + bh;
+    const auto wrs = make_rsrc(p.ws_o + part * Lq * D, (uint32_t)Lq * D * 4);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * nb + 8 * q4 + 4 * g_e;
+        const u32x4 w = {__float_as_uint(oacc[nb][4 * q4]), __float_as_uint(oacc[nb][4 * q4 + 1]),
+                         __float_as_uint(oacc[nb][4 * q4 + 2]), __float_as_uint(oacc[nb][4 * q4 + 3])};
+        buf_store16(wrs, (uint32_t)(row_e * D + d0) * 4, w);
+      }
+    if (g_e == 0 && row_e < Lq) {
+      const u32x4 st = {__float_as_uint(m_run), __float_as_uint(lf_t), __float_as_uint(lr_t), 0u};
+      *(u32x4*)(p.ws_ml + (part * Lq + row_e) * 4) = st;
+    }
+    return;
+  }
+  // one pass: normalise by the sum of the rounded weights, store O and LSE
   const float inv = 1.0f / lr_t;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -601,6 +646,54 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       buf_store8(ors, (uint32_t)(row_e * o_sl + d0) * 2, w);  // rows >= Lq are dropped
     }
   if (g_e == 0 && row_e < Lq) p.lse[(size_t)bh * Lq + row_e] = (m_run + log2f(lf_t)) * 0.69314718055994530942f;
+}
+
+// ---- merge of key splits ([DF §2.2], second layer, applied across splits: the
+// running max and exp-sums of independent key ranges combine exactly).  For row
+// i with split partials (Ô_s, m_s, lf_s, lr_s), all relative to m_s in log2 units:
+//   M = max_s m_s,  w_s = 2^(m_s - M),
+//   O = Σ w_s Ô_s / Σ w_s lr_s,   LSE = (M + log2 Σ w_s lf_s) · ln 2,
+// which is what one pass over all keys computes.  HBM-bound; one row per D/4
+// lanes, 4 dims per lane.
+struct MergeParams {
+  const float* ws_o;
+  const float* ws_ml;
+  void* o;
+  float* lse;
+  int Lq, H, n_split, bh;
+  int64_t o_sb, o_sh;
+  int o_sl;
+};
+
+template <int D, int DT>
+__global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
+  constexpr int LPR = D / 4, RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR;  // row over B*H*Lq
+  const int d0 = (tid % LPR) * 4;
+  if (r >= (int64_t)p.bh * p.Lq) return;
+  const int bh = (int)(r / p.Lq), i = (int)(r - (int64_t)bh * p.Lq);
+  const size_t stride = (size_t)p.bh * p.Lq;  // rows per split
+  float M = -3.0e38f;
+  for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, p.ws_ml[((size_t)s * stride + r) * 4]);
+  float lf = 0.f, lr = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int s = 0; s < p.n_split; ++s) {
+    const size_t row = (size_t)s * stride + r;
+    const f32x4 st = *(const f32x4*)(p.ws_ml + row * 4);
+    const float w = __builtin_amdgcn_exp2f(st[0] - M);
+    lf += w * st[1];
+    lr += w * st[2];
+    const f32x4 x = *(const f32x4*)(p.ws_o + row * D + d0);
+    a0 += w * x[0];
+    a1 += w * x[1];
+    a2 += w * x[2];
+    a3 += w * x[3];
+  }
+  const float inv = 1.0f / lr;
+  const int b = bh / p.H, h = bh - b * p.H;
+  char* const orow = (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)i * p.o_sl + d0) * 2;
+  *(u32x2*)orow = u32x2{pack2<DT>(a0 * inv, a1 * inv), pack2<DT>(a2 * inv, a3 * inv)};
+  if (d0 == 0) p.lse[r] = (M + log2f(lf)) * 0.69314718055994530942f;
 }
 
 }  // namespace fa355
