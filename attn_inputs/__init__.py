@@ -59,6 +59,7 @@ class Workload:
     sigma_q: float = 1.0
     boost: float | None = None   # logit margin of one target key per row (None: no boost)
     description: str = ""
+    splits: int = 1              # key splits the workload is timed with (fa_fwd_splitkv when > 1)
 
     @property
     def scale(self) -> float:
@@ -66,9 +67,20 @@ class Workload:
 
     @property
     def flops(self) -> float:
-        """4·B·H·Lq·Lk·D, halved when causal (the metric's convention)."""
-        f = 4.0 * self.B * self.H * self.Lq * self.Lk * self.D
-        return f / 2 if self.causal else f
+        """4·B·H·Lq·Lk·D, halved when causal (the metric's convention).
+
+        Causal with Lq < Lk (queries aligned with the last Lq keys) counts
+        4·B·H·Lq·(Lk − Lq/2)·D, which is the same convention: Lq = Lk gives half.
+        """
+        if self.causal:
+            return 4.0 * self.B * self.H * self.Lq * (self.Lk - self.Lq / 2) * self.D
+        return 4.0 * self.B * self.H * self.Lq * self.Lk * self.D
+
+    @property
+    def hbm_bytes(self) -> int:
+        """Algorithmic HBM bytes: Q, K, V read once, O written once (dtype), LSE written (fp32)."""
+        return 2 * (2 * self.B * self.H * self.Lq * self.D + 2 * self.B * self.H * self.Lk * self.D) \
+            + 4 * self.B * self.H * self.Lq
 
 
 WORKLOADS: dict[str, Workload] = {
@@ -86,6 +98,26 @@ WORKLOADS: dict[str, Workload] = {
                  description="long sequence: B=1 H=32 L=16384 D=128 bf16 causal"),
     ]
 }
+
+
+# Inference shapes whose query tiles alone leave most of the 256 CUs idle: timed
+# with key splits (fa_fwd_splitkv).  Causal ones align the queries with the last
+# Lq keys (a prefill chunk or a decode step over a KV cache).
+SPLIT_WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("kvcache_16k", 1, 32, 256, 16384, 128, "bf16", False, 1006, splits=8,
+                 description="256 queries over a 16K KV cache: B=1 H=32 Lq=256 Lk=16384 D=128 bf16, 8 key splits"),
+        Workload("decode_32k", 1, 8, 1, 32768, 128, "bf16", True, 1007, splits=32,
+                 description="one decode step over a 32K KV cache: B=1 H=8 Lq=1 Lk=32768 D=128 bf16 causal, "
+                             "32 key splits"),
+        Workload("prefill_chunk_8k", 2, 32, 512, 8192, 128, "bf16", True, 1008, splits=2,
+                 description="a 512-row prefill chunk after 7.7K cached keys: B=2 H=32 Lq=512 Lk=8192 D=128 bf16 "
+                             "causal, 2 key splits"),
+    ]
+}
+
+ALL_WORKLOADS: dict[str, Workload] = {**WORKLOADS, **SPLIT_WORKLOADS}
 
 
 def _torch_dtype(dtype: str):
@@ -151,7 +183,7 @@ def make_inputs(w: Workload | str, seed: int | None = None) -> dict:
     boosted workload) the per-row target key indices as an int64 numpy array.
     """
     if isinstance(w, str):
-        w = WORKLOADS[w]
+        w = ALL_WORKLOADS[w]
     seed = w.seed if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     qs = (w.B, w.H, w.Lq, w.D)

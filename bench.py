@@ -8,7 +8,10 @@
 One step = one ``fa_fwd`` call (the whole hot path: one kernel) over the
 workload's seeded synthetic Q, K, V, which are resident in HBM before timing
 starts.  The metric is attention-forward TFLOP/s with FLOP = 4·B·H·Lq·Lk·D,
-halved for causal, and its fraction of MI355X's dense bf16 MFMA peak.
+halved for causal, and its fraction of MI355X's dense bf16 MFMA peak.  The
+split-KV inference shapes (``--workload kvcache_16k`` and the like) step through
+``fa_fwd_splitkv`` (main kernel plus merge); those below the ridge point report
+an HBM roofline instead.
 
 The shader clock of MI355X ramps over the first few hundred launches of this
 kernel, so the default warm-up is long (a few hundred milliseconds).
@@ -42,7 +45,11 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (bf16 causal, L=4096, D=128) and % of MFMA peak"
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_06_amd", "csrc", f) for f in ("fa_fwd_kernel.hpp", "fa355.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_train7b_4k_traffic.md")
-TRACE_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_train7b_4k_kernel_trace.md")
+
+
+def trace_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"fa_fwd_kernel_{workload}_kernel_trace.md")
+
 COPY_BYTES = 1 << 30  # the plain device copy that calibrates the HBM byte counters
 
 
@@ -103,7 +110,8 @@ def sampled_parity(inp, o, lse, n_rows: int = 128) -> dict:
     w = inp["workload"]
     r = np.random.default_rng(1)
     heads = [(0, 0), (w.B - 1, w.H - 1)]
-    rows = np.unique(np.concatenate([np.arange(16), np.arange(w.Lq - 16, w.Lq), r.integers(0, w.Lq, n_rows)]))
+    rows = np.unique(np.concatenate([np.arange(min(16, w.Lq)), np.arange(max(0, w.Lq - 16), w.Lq),
+                                     r.integers(0, w.Lq, n_rows)]))
     O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, w.causal, rows=rows, heads=heads)
     oc, lc = o.double().cpu().numpy(), lse.double().cpu().numpy()
     eo = max(float(np.abs(oc[b, h][rows] - O_ref[b, h]).max()) for b, h in heads)
@@ -171,7 +179,7 @@ def summarize_traffic(directory: str, w) -> str:
     kw = COPY_BYTES / (sum(cw) / len(cw) * 1024)   # and writes
     fetch = sum(ff) / len(ff) * 1024 * kf
     write = sum(fw) / len(fw) * 1024 * kw
-    alg = 2 * (2 * w.B * w.H * w.Lq * w.D + 2 * w.B * w.H * w.Lk * w.D) + 4 * w.B * w.H * w.Lq
+    alg = w.hbm_bytes
     lines = [
         f"# HBM traffic of fa_fwd_kernel on {w.name} ({w.description})",
         "",
@@ -205,15 +213,16 @@ def summarize_trace(directory: str, w, bench_line: str | None) -> str:
     rows = _csv_rows(directory, "*kernel_stats.csv")
     if not rows:
         raise SystemExit("no kernel_stats.csv under " + directory)
-    keep = [r for r in rows if "fa_fwd_kernel" in r.get("Name", "")]
+    keep = [r for r in rows if "fa_fwd_kernel" in r.get("Name", "") or "fa_merge_kernel" in r.get("Name", "")]
     hdr = list(rows[0].keys())
+    wl = "" if w.name == "train7b_4k" else f" --workload {w.name}"
     lines = [
         f"# rocprofv3 kernel trace: fa_fwd_kernel on {w.name} ({w.description})",
         "",
         "Command (from the repository root on the GPU box):",
         "",
-        "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o t -- python3 bench.py --no-cpu-baseline --no-parity",
-        f"    python3 bench.py --summarize-trace gpurun_out/trace",
+        f"    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o t -- python3 bench.py{wl} --no-cpu-baseline --no-parity",
+        f"    python3 bench.py{wl} --summarize-trace gpurun_out/trace --bench-log <that run's stdout>",
         "",
         "kernel_stats.csv rows for the kernel (durations in ns):",
         "",
@@ -232,7 +241,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", default="train7b_4k")
+    ap.add_argument("--workload", default="train7b_4k",
+                    help="a name from attn_inputs.WORKLOADS or attn_inputs.SPLIT_WORKLOADS")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="key splits (fa_fwd_splitkv when > 1); default: the workload's own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
@@ -249,7 +261,7 @@ def main() -> int:
 
     import attn_inputs
 
-    w = attn_inputs.WORKLOADS[args.workload]
+    w = attn_inputs.ALL_WORKLOADS[args.workload]
     if args.summarize_traffic:
         text = summarize_traffic(args.summarize_traffic, w)
         with open(TRAFFIC_FILE, "w", encoding="utf-8") as f:
@@ -262,7 +274,7 @@ def main() -> int:
             with open(args.bench_log, encoding="utf-8") as f:
                 line = next((x for x in f if x.startswith("{")), None)
         text = summarize_trace(args.summarize_trace, w, line)
-        with open(TRACE_FILE, "w", encoding="utf-8") as f:
+        with open(trace_file(w.name), "w", encoding="utf-8") as f:
             f.write(text)
         print(text)
         return 0
@@ -281,9 +293,17 @@ def main() -> int:
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    splits = w.splits if args.splits is None else args.splits
+    if splits > 1:
+        ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.Lq, w.D, splits), dtype=torch.uint8,
+                         device=dev)
 
-    def step():
-        fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, stream=stream)
+        def step():
+            fa.fa_fwd_splitkv(q, k, v, o, lse, causal=w.causal, scale=w.scale, num_splits=splits, workspace=ws,
+                              stream=stream)
+    else:
+        def step():
+            fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -306,9 +326,22 @@ def main() -> int:
     log(f"bench: {args.steps} steps in {wall * 1e3:.2f} ms; kernel mean {mean_kernel_s * 1e6:.1f} us "
         f"(min {min(kernel_ms) * 1e3:.1f} us); {achieved:.1f} TFLOP/s = {100 * achieved / PEAK_BF16_TFLOPS:.2f}% of peak")
 
-    traffic = committed_traffic(w.name)
+    traffic = committed_traffic(w.name) if splits == 1 else None
+    kname = f"fa_fwd_kernel<{w.D},{'bf16' if w.dtype == 'bf16' else 'f16'},{'causal' if w.causal else 'full'}>"
+    if splits > 1:
+        kname += " + fa_merge_kernel (the events bracket both)"
+    # below the ridge point (peak flop/s over peak bytes/s) the HBM roofline bounds the step
+    if w.flops / w.hbm_bytes >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 5)}
+    else:
+        gbs = w.hbm_bytes / mean_kernel_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 5), "tflops": round(achieved, 3)}
+    roof.update({"traffic": traffic, "kernel": kname, "mean_launch_us": round(mean_kernel_s * 1e6, 3),
+                 "algorithmic_bytes": w.hbm_bytes})
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "train7b_4k" else f"attention fwd TFLOP/s ({w.description})",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -321,13 +354,9 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "D": w.D, "causal": w.causal,
-                   "scale": w.scale, "seed": w.seed, "flop_per_step": w.flops},
+                   "scale": w.scale, "seed": w.seed, "num_splits": splits, "flop_per_step": w.flops},
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 5), "traffic": traffic,
-                     "kernel": f"fa_fwd_kernel<{w.D},{'bf16' if w.dtype == 'bf16' else 'f16'},"
-                               f"{'causal' if w.causal else 'full'}>",
-                     "mean_launch_us": round(mean_kernel_s * 1e6, 3)},
+        "roofline": roof,
     }
     if not args.no_parity:
         out["parity"] = sampled_parity(inp, o, lse)

@@ -252,6 +252,10 @@ def test_splitkv_partial_slab_limit():
 
 def test_suggest_num_splits():
     assert fa.suggest_num_splits(4, 32, 4096, 4096, 128, True) == 1        # 2,048 workgroups fill 256 CUs
-    assert fa.suggest_num_splits(1, 32, 2048, 2048, 128, True) == 2        # 256 workgroups, causal
+    assert fa.suggest_num_splits(1, 32, 2048, 2048, 128, True) == 1        # 256 workgroups already
+    assert fa.suggest_num_splits(1, 8, 1, 32768, 128, False) == 32         # decode: 8 workgroups
+    assert fa.suggest_num_splits(1, 32, 256, 16384, 128, False) == 8       # 32 workgroups
+    assert fa.suggest_num_splits(2, 32, 512, 8192, 128, True) == 2         # 128 workgroups
+    assert fa.suggest_num_splits(1, 32, 1024, 1024, 64, True) == 1         # 8 tiles on average
     assert fa.suggest_num_splits(1, 1, 128, 128, 64, False) == 1           # too few keys to split
     assert 1 <= fa.suggest_num_splits(1, 2, 256, 65536, 128, False) <= 64

@@ -74,6 +74,19 @@ def test_workload_table():
     assert math.isclose(w["train7b_4k"].flops, 4 * 4 * 32 * 4096 * 4096 * 128 / 2)
 
 
+def test_split_workload_flops_and_bytes():
+    s = ai.SPLIT_WORKLOADS
+    assert set(s) == {"kvcache_16k", "decode_32k", "prefill_chunk_8k"} and not set(s) & set(ai.WORKLOADS)
+    # causal with Lq < Lk: row i sees Lk - Lq + i + 1 keys; the count is Lq·(Lk - Lq/2) + Lq/2
+    w = s["prefill_chunk_8k"]
+    pairs = sum(w.Lk - w.Lq + i + 1 for i in range(w.Lq))
+    assert math.isclose(w.flops, 4 * w.B * w.H * w.D * (pairs - w.Lq / 2))
+    d = s["decode_32k"]
+    assert math.isclose(d.flops, 4 * 8 * 32768 * 128 - 4 * 8 * 128 / 2)
+    assert d.hbm_bytes == 2 * (2 * 8 * 128 + 2 * 8 * 32768 * 128) + 4 * 8
+    assert ai.make_inputs("decode_32k")["q"].shape == (1, 8, 1, 128)
+
+
 def test_boost_margin_after_rounding():
     """A reduced stress workload (same recipe, L=1024): each row's target logit leads every other
     logit by about 20 after Q is rounded to bf16; targets cover the key range."""
