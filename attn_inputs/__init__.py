@@ -211,6 +211,13 @@ def make_inputs(w: Workload | str, seed: int | None = None) -> dict:
     return dict(q=q, k=k, v=v, scale=w.scale, causal=w.causal, dtype=w.dtype, workload=w, targets=targets)
 
 
+def make_dout(shape, dtype: str, seed: int, sigma: float = 1.0):
+    """An upstream gradient dO for the backward pass: standard normal × sigma over ``shape`` in C
+    order from PCG64(seed), rounded as Q, K, V are.  Returns a CPU torch tensor."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return round_to(draw_normal(rng, tuple(shape)) * sigma, dtype)
+
+
 def make_custom(B: int, H: int, Lq: int, Lk: int, D: int, dtype: str, causal: bool, seed: int,
                 sigma_q: float = 1.0, sigma_k: float = 1.0, sigma_v: float = 1.0) -> dict:
     """Same recipe for an arbitrary shape (parity edge cases)."""

@@ -63,7 +63,7 @@ typedef enum {
   FA_ERR_LAUNCH = -9,       /* the kernel launch failed (HIP code in fa_last_hip_error())        */
   FA_ERR_STRIDE = -10,      /* fa_fwd_strided: a stride < 0, or a row stride < D                 */
   FA_ERR_SPLITS = -11,      /* fa_fwd_splitkv: num_splits outside 1..64                          */
-  FA_ERR_WORKSPACE = -12    /* fa_fwd_splitkv: workspace smaller than the size query returns     */
+  FA_ERR_WORKSPACE = -12    /* fa_fwd_splitkv / fa_bwd: workspace smaller than its size query    */
 } fa_status;
 
 /*
@@ -152,6 +152,53 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
                    const int64_t* o_stride, float scale, int causal, int dtype, int num_splits, void* workspace,
                    size_t workspace_bytes, fa_stream_t stream);
+
+/*
+ * fa_bwd — enqueue the attention backward pass on `stream`: the gradients of
+ * o (the forward operation above) with respect to q, k and v for an upstream
+ * gradient dout of o.
+ *
+ * [DF §2.2] (third layer, recomputation): no score matrix is stored; the score
+ * tiles are recomputed from q and k, and the probabilities from the forward
+ * pass's lse: P_ij = exp(s_ij - lse_i) on visible pairs (the same visibility
+ * rule as fa_fwd, including causal with Lq <= Lk).  The gradients are those of
+ * the forward definition:
+ *
+ *     dv_j  = sum_i P_ij dout_i
+ *     dS_ij = P_ij * (dout_i . v_j - D_i),   D_i = dout_i . o_i
+ *     dq_i  = scale * sum_j dS_ij k_j,       dk_j = scale * sum_i dS_ij q_i
+ *
+ * (D_i = sum_j P_ij (dout_i . v_j) because the row of P sums to one.)
+ *
+ *   q, o, dout [B, H, Lq, D]   dense row-major, `dtype`, read only; o and lse
+ *                              must be the outputs of fa_fwd on the same q, k,
+ *                              v, scale and causal flag.
+ *   k, v       [B, H, Lk, D]   dense row-major, `dtype`, read only.
+ *   lse        [B, H, Lq]      fp32, natural log (fa_fwd's output), read only.
+ *   dq         [B, H, Lq, D]   written, `dtype` (rounded to nearest even).
+ *   dk, dv     [B, H, Lk, D]   written, `dtype`.
+ *   workspace                  at least fa_bwd_workspace_size(B, H, Lq) bytes,
+ *                              256-byte aligned, device memory owned by the
+ *                              caller (2 fp32 values per query row, rows
+ *                              padded to a multiple of 4), written
+ *                              by the call; calls sharing one workspace must be
+ *                              ordered on one stream.
+ *   B, H, Lq, Lk, D, scale, causal, dtype, stream: as for fa_fwd.
+ *
+ * dq, dk, dv must not overlap each other or the inputs.  q, k, v, o, dout, dq,
+ * dk, dv must be 16-byte aligned (FA_ERR_ALIGN), lse 4-byte aligned.  Every
+ * pointer is required (FA_ERR_NULL).  Limits: (L + 256)*D*2 < 2^32 bytes for
+ * L = Lq and L = Lk (FA_ERR_SHAPE).  Three kernels are enqueued (row
+ * statistics, dq, then dk and dv); the call returns without synchronising.
+ * Precision: fp32 accumulation; P and dS are rounded to `dtype` as matrix-core
+ * operands.  Each output element is written by exactly one thread, in a fixed
+ * order, so results are bitwise reproducible.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int Lq);
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, fa_stream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);

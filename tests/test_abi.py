@@ -49,7 +49,8 @@ def call_strided(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, Lq=64, Lk=6
 
 def test_header_declares_the_abi():
     assert declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-                                    "fa_status_string", "fa_last_hip_error", "fa_version"]
+                                    "fa_bwd_workspace_size", "fa_bwd", "fa_status_string", "fa_last_hip_error",
+                                    "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -64,7 +65,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert fa.fa_version() == 10200
+    assert fa.fa_version() == 10300
     for code in range(0, -13, -1):
         s = fa.fa_status_string(code)
         assert s and "unknown" not in s
@@ -259,3 +260,54 @@ def test_suggest_num_splits():
     assert fa.suggest_num_splits(1, 32, 1024, 1024, 64, True) == 1         # 8 tiles on average
     assert fa.suggest_num_splits(1, 1, 128, 128, 64, False) == 1           # too few keys to split
     assert 1 <= fa.suggest_num_splits(1, 2, 256, 65536, 128, False) <= 64
+
+
+# ------------------------------------------------------------------------------------------
+# fa_bwd: argument checks (nothing is launched on these paths)
+# ------------------------------------------------------------------------------------------
+
+PB = [0x100000 * (i + 1) for i in range(10)]  # q k v o dout lse dq dk dv workspace (256-byte aligned)
+
+
+def call_bwd(B=1, H=2, Lq=300, Lk=500, D=128, scale=0.125, causal=0, dtype=1, ws_bytes=None, ptrs=None):
+    p = dict(zip(["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"], PB))
+    p.update(ptrs or {})
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_size(B, H, Lq)
+    return fa.lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["dout"], p["lse"], p["dq"], p["dk"], p["dv"],
+                         B, H, Lq, Lk, D, scale, causal, dtype, p["ws"], ws_bytes, None)
+
+
+def test_bwd_workspace_size():
+    # LSE·log2(e), then Δ: fp32 per query row each, the second array 256-byte aligned
+    assert fa.fa_bwd_workspace_size(2, 3, 100) == 2560 + 2400
+    assert fa.fa_bwd_workspace_size(1, 1, 64) == 256 + 256
+    assert fa.fa_bwd_workspace_size(1, 1, 5) == 256 + 8 * 4          # rows padded to a multiple of 4
+    assert fa.fa_bwd_workspace_size(0, 1, 64) == 0 and fa.fa_bwd_workspace_size(1, 1, 0) == 0
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"])
+def test_bwd_null_pointers(which):
+    assert call_bwd(ptrs={which: None}) == -1
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "dout", "dq", "dk", "dv"])
+def test_bwd_alignment(which):
+    base = dict(zip(["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"], PB))
+    assert call_bwd(ptrs={which: base[which] + 8}) == -5
+    assert call_bwd(ptrs={which: base[which] + 16}, scale=float("inf")) == -6  # 16 bytes is enough
+
+
+def test_bwd_argument_checks():
+    assert call_bwd(ptrs={"lse": PB[5] + 2}) == -5
+    assert call_bwd(ptrs={"ws": PB[9] + 16}) == -5       # workspace needs 256-byte alignment
+    assert call_bwd(B=0) == -2 and call_bwd(Lk=0) == -2
+    assert call_bwd(D=96) == -3
+    assert call_bwd(dtype=2) == -4
+    assert call_bwd(scale=float("nan")) == -6
+    assert call_bwd(causal=1, Lq=501, Lk=500) == -7
+    need = fa.fa_bwd_workspace_size(1, 2, 300)
+    assert call_bwd(ws_bytes=need - 1) == -12
+    assert call_bwd(Lk=16_776_960) == -2                 # slab beyond 32-bit offsets
+    # enough of everything: a later check fails, so nothing launches
+    assert call_bwd(ws_bytes=need, causal=1, Lq=600, Lk=500) == -7

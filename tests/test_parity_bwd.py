@@ -1,0 +1,146 @@
+"""GPU parity of the backward pass (fa_bwd through the C ABI) against the fp64 gradient oracle.
+
+The GPU backward takes o and lse from the GPU forward pass on the same rounded
+q, k, v; the oracle differentiates the definition in fp64 from q, k, v and dO
+alone.  Bar, per (batch, head) slab and per gradient g ∈ {dq, dk, dv}:
+
+    max |g_gpu − g_ref| ≤ TOL · max |g_ref|    and    rms(g_gpu − g_ref) ≤ TOL_RMS · rms(g_ref)
+
+with TOL = 1e-2 (bf16) / 2e-3 (fp16) and TOL_RMS = 6e-3 / 8e-4, plus an absolute
+1e-5 for slabs whose exact gradient is 0 (one visible key: the kernel's dP − Δ is
+then an fp32 rounding residue, ~1e-7 at unit-scale inputs).  Derivation: the
+kernels round P and dS to the input type as matrix-core operands and round the
+outputs; emulating exactly those roundings on the CPU (fp64 otherwise) gives at
+most 4.4e-3 / 5.5e-4 of the slab's max and 2.5e-3 / 3.1e-4 of its rms, at
+L = 300..1024, D = 64 and 128, causal and not.  The bars are 2.3–3.6x those.
+Outputs are pre-filled with NaN so that an unwritten element fails.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import tiled_attention_06_amd as fa
+from oracle import attention_bwd_fp64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp16": 2e-3, "bf16": 1e-2}
+TOL_RMS = {"fp16": 8e-4, "bf16": 6e-3}
+ABS = 1e-5
+DEV = "cuda:0"
+
+
+def note(msg: str):
+    print(msg, flush=True)
+
+
+def run_bwd(inp, do, causal, scale=None):
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    dod = do.to(DEV)
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    fa.fa_bwd(q, k, v, o, dod, lse, dq, dk, dv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def compare(got, ref, dtype, what, heads=None):
+    names = ("dq", "dk", "dv")
+    for name, g, r in zip(names, got, ref):
+        g = g.double().numpy()
+        pairs = heads if heads is not None else [(b, h) for b in range(g.shape[0]) for h in range(g.shape[1])]
+        for b, h in pairs:
+            gs, rs = g[b, h], r[b, h]
+            assert np.isfinite(gs).all(), f"{what} {name} ({b},{h}): non-finite (unwritten?)"
+            err = np.abs(gs - rs)
+            mx, rms = np.abs(rs).max(), np.sqrt((rs ** 2).mean())
+            e_max, e_rms = err.max(), np.sqrt((err ** 2).mean())
+            note(f"  {what} {name} ({b},{h}): max err {e_max:.3e} (max |ref| {mx:.3e}), rms err {e_rms:.3e} "
+                 f"(rms ref {rms:.3e})")
+            assert e_max <= TOL[dtype] * mx + ABS, f"{what} {name} ({b},{h}): max err {e_max} > {TOL[dtype]} * {mx}"
+            assert e_rms <= TOL_RMS[dtype] * rms + ABS, f"{what} {name} ({b},{h}): rms err {e_rms} > {TOL_RMS[dtype]} * {rms}"
+
+
+CASES = [  # B, H, Lq, Lk, D, dtype, causal
+    (1, 2, 64, 64, 64, "bf16", False), (1, 2, 300, 300, 128, "bf16", True), (2, 3, 257, 257, 64, "fp16", True),
+    (1, 2, 100, 1000, 128, "fp16", True), (1, 2, 1000, 100, 64, "bf16", False), (1, 1, 1, 1, 128, "bf16", False),
+    (1, 1, 1, 1, 64, "fp16", True), (1, 2, 129, 65, 128, "fp16", False), (1, 1, 513, 513, 128, "bf16", True),
+    (1, 2, 200, 333, 64, "bf16", True), (1, 1, 640, 640, 128, "fp16", False),
+]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal", CASES,
+                         ids=[f"B{b}H{h}_{lq}x{lk}_D{d}_{dt}_{'c' if c else 'nc'}" for b, h, lq, lk, d, dt, c in CASES])
+def test_bwd_matches_oracle(B, H, Lq, Lk, D, dtype, causal):
+    inp = ai.make_custom(B, H, Lq, Lk, D, dtype, causal, seed=50_000 + Lq + 3 * Lk + D)
+    do = ai.make_dout((B, H, Lq, D), dtype, seed=60_000 + Lq + Lk)
+    note(f"bwd B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype} causal={causal}")
+    got = run_bwd(inp, do, causal)
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, inp["scale"], causal)
+    compare(got, ref, dtype, "bwd")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.35])
+def test_bwd_scale_values(scale):
+    inp = ai.make_custom(1, 2, 200, 260, 64, "bf16", True, seed=70_001)
+    do = ai.make_dout((1, 2, 200, 64), "bf16", seed=70_002)
+    note(f"bwd scale {scale}")
+    got = run_bwd(inp, do, True, scale=scale)
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, scale, True)
+    if scale == 0.0:
+        assert float(got[0].abs().max()) == 0.0 and float(got[1].abs().max()) == 0.0  # dq = dk = 0 exactly
+        g, r = got[2].double().numpy(), ref[2]
+        assert np.abs(g - r).max() <= TOL["bf16"] * np.abs(r).max()
+    else:
+        compare(got, ref, "bf16", f"bwd scale {scale}")
+
+
+def test_bwd_sum_rules_at_train_shape():
+    # 7B 4K training shape: every row of P sums to one (Σ_j dV_j = Σ_i dO_i) and the key-shift
+    # invariance (Σ_j dK_j = 0) hold on every head; two heads against the oracle in full
+    w = ai.WORKLOADS["train7b_4k"]
+    inp = ai.make_inputs(w)
+    do = ai.make_dout((w.B, w.H, w.Lq, w.D), w.dtype, seed=80_003)
+    note("bwd train7b_4k: GPU")
+    got = run_bwd(inp, do, True)
+    dv_sum = got[2].double().sum(dim=2)
+    do_sum = do.double().sum(dim=2)
+    rel = ((dv_sum - do_sum).abs().max() / do_sum.abs().max()).item()
+    note(f"  sum rule dV: {rel:.2e}")
+    assert rel <= 1e-2
+    dk_sum = got[1].double().sum(dim=2).abs().max().item()
+    dk_scale = got[1].double().abs().sum(dim=2).max().item()
+    note(f"  sum rule dK: {dk_sum:.3e} of {dk_scale:.3e}")
+    assert dk_sum <= 1e-2 * dk_scale
+    heads = [(0, 0), (3, 31)]
+    note("bwd train7b_4k: oracle on two heads")
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, w.scale, True, heads=heads)
+    compare(got, ref, w.dtype, "bwd train7b_4k", heads=heads)
+
+
+def test_bwd_deterministic():
+    inp = ai.make_custom(1, 4, 700, 700, 128, "bf16", True, seed=90_001)
+    do = ai.make_dout((1, 4, 700, 128), "bf16", seed=90_002)
+    a = run_bwd(inp, do, True)
+    b = run_bwd(inp, do, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_flash_attention_autograd():
+    inp = ai.make_custom(2, 2, 320, 320, 64, "fp16", True, seed=91_001)
+    do = ai.make_dout((2, 2, 320, 64), "fp16", seed=91_002)
+    q, k, v = (inp[n].to(DEV).requires_grad_(True) for n in ("q", "k", "v"))
+    o = fa.flash_attention(q, k, v, causal=True)
+    o.backward(do.to(DEV))
+    torch.cuda.synchronize()
+    got = (q.grad.cpu(), k.grad.cpu(), v.grad.cpu())
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, inp["scale"], True)
+    compare(got, ref, "fp16", "autograd")
+    direct = run_bwd(inp, do, True)
+    for x, y in zip(got, direct):
+        assert torch.equal(x, y)

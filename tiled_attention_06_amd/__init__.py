@@ -1,4 +1,4 @@
-"""Python binding of libfa355, the gfx950 fused attention forward pass.
+"""Python binding of libfa355, the gfx950 fused attention forward and backward passes.
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernel behind the C ABI declared in ``include/fa355.h``.  PyTorch supplies
@@ -7,8 +7,10 @@ library is missing, importing this package raises ImportError.
 
 Names follow the C ABI: ``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_status_string``, ``fa_last_hip_error``,
-``fa_version``; ``fa_fwd_qkvpacked`` is a view helper over ``fa_fwd_strided`` for
-a packed [B, L, 3, H, D] qkv buffer, and ``suggest_num_splits`` a host heuristic.
+``fa_version``, ``fa_bwd``, ``fa_bwd_workspace_size``; ``fa_fwd_qkvpacked`` is a
+view helper over ``fa_fwd_strided`` for a packed [B, L, 3, H, D] qkv buffer,
+``suggest_num_splits`` a host heuristic, and ``flash_attention`` an autograd
+function whose forward is ``fa_fwd`` and whose backward is ``fa_bwd``.
 """
 
 from __future__ import annotations
@@ -20,8 +22,8 @@ import os
 import torch
 
 __all__ = ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_qkvpacked",
-           "suggest_num_splits", "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH",
-           "FA_DTYPE_F16", "FA_DTYPE_BF16"]
+           "suggest_num_splits", "fa_bwd", "fa_bwd_workspace_size", "flash_attention", "fa_status_string",
+           "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH", "FA_DTYPE_F16", "FA_DTYPE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
 
@@ -46,6 +48,10 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [vp] * 9 + [i] * 5 + [ctypes.c_float, i, i, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -210,3 +216,71 @@ def fa_fwd_qkvpacked(qkv: torch.Tensor, o: torch.Tensor | None = None, lse: torc
         raise ValueError("o must be [B, L, H, D]")
     _, lse = fa_fwd_strided(q, k, v, o.transpose(1, 2), lse, causal=causal, scale=scale, stream=stream)
     return o, lse
+
+
+def fa_bwd_workspace_size(B: int, H: int, Lq: int) -> int:
+    """Bytes of workspace ``fa_bwd`` needs (0 for invalid arguments)."""
+    return int(lib.fa_bwd_workspace_size(B, H, Lq))
+
+
+def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+           lse: torch.Tensor, dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+           dv: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
+           workspace: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """Enqueue the attention backward pass (the C ``fa_bwd``): gradients of o = fa_fwd(q, k, v) for dout.
+
+    q, o, dout: [B, H, Lq, D]; k, v: [B, H, Lk, D]; lse: [B, H, Lq] float32 (fa_fwd's outputs o and lse
+    for the same q, k, v, scale and causal flag).  All dense (contiguous).  dq, dk, dv are allocated when
+    not given; ``workspace`` (at least ``fa_bwd_workspace_size`` bytes) likewise.  Returns (dq, dk, dv).
+    """
+    B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
+    if tuple(dout.shape) != tuple(q.shape) or dout.dtype != q.dtype or dout.device != q.device:
+        raise ValueError("dout must be a tensor of q's shape, dtype and device")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be a tensor of {name[1:]}'s shape, dtype and device")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if not t.is_contiguous():
+            raise ValueError(f"fa_bwd takes dense [B, H, L, D] tensors: {name} is not contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    need = fa_bwd_workspace_size(B, H, Lq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    code = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D, float(scale),
+                      1 if causal else 0, _DTYPES[q.dtype], workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if code != 0:
+        raise FaError(code)
+    return dq, dk, dv
+
+
+class _FlashAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        q, k, v = (t.contiguous() for t in (q, k, v))
+        o, lse = fa_fwd(q, k, v, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale = causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = fa_bwd(q, k, v, o, do.contiguous(), lse, causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def flash_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                    scale: float | None = None) -> torch.Tensor:
+    """o = softmax(scale·q·kᵀ [causal]) · v on [B, H, L, D] tensors, differentiable in q, k and v.
+
+    The forward pass is ``fa_fwd`` (o and the per-row LSE are kept), the backward pass ``fa_bwd``.
+    """
+    return _FlashAttention.apply(q, k, v, causal, scale)

@@ -1,9 +1,10 @@
-// libfa355: C ABI around the gfx950 attention forward kernel.
+// libfa355: C ABI around the gfx950 attention forward and backward kernels.
 //
 // Argument validation happens here, on the host, before any HIP call, so every
 // FA_ERR_* of a bad argument can be produced without a GPU.  A valid call
 // selects the kernel instance for (head dim, dtype, causal) and enqueues one
-// launch on the caller's stream (two with key splits: partials, then the merge).
+// launch on the caller's stream (two with key splits: partials, then the merge;
+// three for the backward pass: row statistics, dQ, then dK and dV).
 // No allocation, no synchronisation, no global mutable state apart from the
 // per-thread last HIP error.
 
@@ -13,13 +14,14 @@
 #include <hip/hip_runtime.h>
 
 #include "fa355.h"
+#include "fa_bwd_kernel.hpp"
 #include "fa_fwd_kernel.hpp"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
 constexpr int kMaxSplits = 64;
 
 int launch_status() {
@@ -137,6 +139,93 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   return D == 128 ? dispatch_dtype<128>(p, m, dtype, causal != 0, s) : dispatch_dtype<64>(p, m, dtype, causal != 0, s);
 }
 
+// ---- backward
+
+constexpr int kBwdDqRows = 256;   // query rows per dQ workgroup
+constexpr int kBwdKvKeys = 128;   // keys per dK/dV workgroup
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// workspace: LSE·log2(e), then Δ, fp32 [B*H][Lq4] each with Lq4 = Lq rounded up to
+// a multiple of 4 (the second array 256-byte aligned)
+size_t lq4(int Lq) { return ((size_t)Lq + 3) & ~(size_t)3; }
+size_t bwd_ws_bytes(int B, int H, int Lq) {
+  return align256((size_t)B * H * lq4(Lq) * 4) + (size_t)B * H * lq4(Lq) * 4;
+}
+
+template <int D, int DT, bool CAUSAL>
+int launch_bwd(fa355::BwdParams p, hipStream_t stream) {
+  constexpr int rows_per_block = 256 / (D / 8);
+  const int64_t rows = (int64_t)p.bh * p.Lq4;
+  hipLaunchKernelGGL((fa355::fa_bwd_prep_kernel<D, DT>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+                     dim3(256), 0, stream, p);
+  int st = launch_status();
+  if (st != FA_OK) return st;
+  p.num_wg = p.bh * p.n_qt;
+  p.xcd_remap = (p.num_wg % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((fa355::fa_bwd_dq_kernel<D, DT, CAUSAL>), dim3(p.num_wg), dim3(512), 0, stream, p);
+  st = launch_status();
+  if (st != FA_OK) return st;
+  p.num_wg = p.bh * p.n_kt;
+  p.xcd_remap = (p.num_wg % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((fa355::fa_bwd_dkdv_kernel<D, DT, CAUSAL>), dim3(p.num_wg), dim3(256), 0, stream, p);
+  return launch_status();
+}
+
+template <int D>
+int dispatch_bwd(const fa355::BwdParams& p, int dtype, bool causal, hipStream_t s) {
+  if (dtype == FA_DTYPE_BF16)
+    return causal ? launch_bwd<D, fa355::DT_BF16, true>(p, s) : launch_bwd<D, fa355::DT_BF16, false>(p, s);
+  return causal ? launch_bwd<D, fa355::DT_F16, true>(p, s) : launch_bwd<D, fa355::DT_F16, false>(p, s);
+}
+
+int bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+        void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal, int dtype, void* ws,
+        size_t ws_size, fa_stream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !ws) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  const void* p16[8] = {q, k, v, o, dout, dq, dk, dv};
+  for (int i = 0; i < 8; ++i)
+    if (!aligned(p16[i], 16)) return FA_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(ws, 256)) return FA_ERR_ALIGN;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (causal && Lq > Lk) return FA_ERR_CAUSAL_SHAPE;
+  if (ws_size < bwd_ws_bytes(B, H, Lq)) return FA_ERR_WORKSPACE;
+  // one head's slab plus a tile of padding in 32-bit byte offsets
+  if (((int64_t)Lq + 256) * D * 2 >= (1ll << 32) || ((int64_t)Lk + 256) * D * 2 >= (1ll << 32)) return FA_ERR_SHAPE;
+  const int64_t n_qt = ((int64_t)Lq + kBwdDqRows - 1) / kBwdDqRows;
+  const int64_t n_kt = ((int64_t)Lk + kBwdKvKeys - 1) / kBwdKvKeys;
+  if ((int64_t)B * H >= (1ll << 31) || (int64_t)B * H * n_qt >= (1ll << 22) || (int64_t)B * H * n_kt >= (1ll << 22))
+    return FA_ERR_SHAPE;
+
+  fa355::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.ws_lse2 = (float*)ws;
+  p.ws_delta = (float*)((char*)ws + align256((size_t)B * H * lq4(Lq) * 4));
+  p.Lq = Lq;
+  p.Lq4 = (int)lq4(Lq);
+  p.Lk = Lk;
+  p.bh = (int)((int64_t)B * H);
+  p.kv_off = Lk - Lq;
+  p.n_qt = (int)n_qt;
+  p.n_kt = (int)n_kt;
+  p.num_wg = 0;
+  p.xcd_remap = 0;
+  p.c = (float)((double)scale * 1.4426950408889634074);
+  p.scale = scale;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return D == 128 ? dispatch_bwd<128>(p, dtype, causal != 0, s) : dispatch_bwd<64>(p, dtype, causal != 0, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,10 +258,22 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
              num_splits, workspace, workspace_bytes, stream);
 }
 
+size_t fa_bwd_workspace_size(int B, int H, int Lq) {
+  if (B < 1 || H < 1 || Lq < 1) return 0;
+  return bwd_ws_bytes(B, H, Lq);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, fa_stream_t stream) {
+  return bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Lq, Lk, D, scale, causal, dtype, workspace, workspace_bytes,
+             stream);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
-    case FA_ERR_NULL: return "fa_fwd: a required pointer (q, k, v, o or lse) is NULL";
+    case FA_ERR_NULL: return "a required pointer is NULL (q, k, v, o, lse; dout, dq, dk, dv or workspace for fa_bwd)";
     case FA_ERR_SHAPE: return "fa_fwd: B, H, Lq and Lk must be >= 1 and within the size limits";
     case FA_ERR_HEAD_DIM: return "fa_fwd: head dimension D must be 64 or 128";
     case FA_ERR_DTYPE: return "fa_fwd: dtype must be FA_DTYPE_F16 (0) or FA_DTYPE_BF16 (1)";
@@ -183,7 +284,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_LAUNCH: return "fa_fwd: kernel launch failed (see fa_last_hip_error)";
     case FA_ERR_STRIDE: return "fa_fwd: strides must be >= 0, with a row stride of at least D";
     case FA_ERR_SPLITS: return "fa_fwd_splitkv: num_splits must be between 1 and 64";
-    case FA_ERR_WORKSPACE: return "fa_fwd_splitkv: workspace smaller than fa_fwd_splitkv_workspace_size()";
+    case FA_ERR_WORKSPACE: return "workspace smaller than the size query returns (fa_fwd_splitkv / fa_bwd)";
     default: return "fa_fwd: unknown status code";
   }
 }

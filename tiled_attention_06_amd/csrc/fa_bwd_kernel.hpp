@@ -1,0 +1,448 @@
+// Attention backward kernels for gfx950 (MI355X): dQ, dK, dV by recomputing the
+// probabilities from the forward pass's per-row log-sum-exp.
+//
+// Pages cited (title, then the section on that page):
+//   [DF] "FlashAttention数据流优化：MI50显存与带宽瓶颈实战"  (kwkr.cn/news/544806)
+//
+// [DF §2.2] (third layer, recomputation): the backward pass stores no score
+// matrix; it recomputes the score blocks from Q and K in the forward pass's
+// block order with the softmax statistics the forward pass kept (here the LSE).
+// The gradients are those of the forward definition: with s = scale·q·k,
+// P = exp(s − LSE) on visible pairs, for an upstream gradient dO of O:
+//   dV_j = Σ_i P_ij dO_i,  dP_ij = dO_i·v_j,  Δ_i = Σ_j P_ij dP_ij = dO_i·O_i,
+//   dS_ij = P_ij (dP_ij − Δ_i),  dQ_i = scale Σ_j dS_ij k_j,  dK_j = scale Σ_i dS_ij q_i.
+//
+// Three kernels on one stream:
+//   * fa_bwd_prep_kernel: per row, Δ = dO·O (fp32 from the stored values) and
+//     LSE·log2(e), into the workspace;
+//   * fa_bwd_dq_kernel: one workgroup = 8 waves = 256 query rows (as the forward
+//     pass); per 64-key tile Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ on MFMA (Q and dO rows
+//     resident in VGPRs as B operands), P and dS in registers (one row per lane),
+//     dQᵀ += Kᵀ·dSᵀ with Kᵀ read through transposing LDS reads;
+//   * fa_bwd_dkdv_kernel: one workgroup = 4 waves = 128 keys, each wave owns 32
+//     keys (K and V rows resident in VGPRs); per 64-row query tile S = Q·Kᵀ and
+//     dP = dO·Vᵀ on MFMA, P and dS in registers (one key per lane), then
+//     dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS with dOᵀ and Qᵀ read transposed from LDS.
+// Each tile reaches LDS through the buffer unit (buffer_load ... lds, no VGPR
+// staging) in the forward pass's two LDS images: a row image for operands read
+// row by row and a transposing image for operands read across rows.  Two
+// stages: the copies of the next tile are issued before the current one is
+// computed.  Every wave owns disjoint outputs, so there are no atomics and the
+// results are deterministic.
+//
+// Numerics: fp32 accumulation; P and dS are rounded to the input type as MFMA
+// operands; dQ and dK are scaled in fp32 before the final rounding.
+
+#pragma once
+
+#include "fa_fwd_kernel.hpp"
+
+namespace fa355 {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;   // forward LSE, natural log, fp32 [B*H][Lq]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws_lse2;     // LSE·log2(e), fp32 [B*H][Lq4] (rows Lq..Lq4-1 hold 0)
+  float* ws_delta;    // Δ = dO·O, fp32 [B*H][Lq4] (rows Lq..Lq4-1 hold 0)
+  int Lq, Lk;
+  int Lq4;            // Lq rounded up to a multiple of 4: 16-byte groups of rows never straddle the end
+  int bh;             // B*H
+  int kv_off;         // causal: key position of query row 0 (Lk - Lq >= 0)
+  int n_qt;           // query tiles of 256 rows per head (dq kernel)
+  int n_kt;           // key tiles of 128 keys per head (dkdv kernel)
+  int num_wg;         // workgroups of the kernel being launched
+  int xcd_remap;      // 1: group consecutive work items on one XCD
+  float c;            // scale·log2(e) (any sign)
+  float scale;
+};
+
+// The two 16-bit values of a dword as fp32 (exact), low half first.
+template <int DT>
+__device__ __forceinline__ float2 unpack2(uint32_t u) {
+  if constexpr (DT == DT_BF16)
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+  else
+    return make_float2((float)__builtin_bit_cast(_Float16, (unsigned short)(u & 0xffffu)),
+                       (float)__builtin_bit_cast(_Float16, (unsigned short)(u >> 16)));
+}
+
+// Δ_i = Σ_d dO_id·O_id and LSE_i·log2(e), per head padded with zero rows to Lq4.
+// D/8 lanes per row, 16-byte loads.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int64_t w = (int64_t)blockIdx.x * RPB + tid / LPR;  // row over B*H*Lq4
+  const int c0 = (tid % LPR) * 8;
+  const int64_t total = (int64_t)p.bh * p.Lq4;
+  const int64_t bh = w / p.Lq4, i = w - bh * p.Lq4;
+  const bool real = w < total && i < p.Lq;
+  const int64_t r = bh * p.Lq + i;  // the row in o, dout and lse
+  float acc = 0.f;
+  if (real) {
+    const u32x4 a = *(const u32x4*)((const char*)p.o + (r * D + c0) * 2);
+    const u32x4 b = *(const u32x4*)((const char*)p.dout + (r * D + c0) * 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float2 x = unpack2<DT>(a[e]), y = unpack2<DT>(b[e]);
+      acc = __builtin_fmaf(x.x, y.x, acc);
+      acc = __builtin_fmaf(x.y, y.y, acc);
+    }
+  }
+  // sum over the LPR lanes of the row (aligned groups within the wave)
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (w < total && tid % LPR == 0) {
+    p.ws_delta[w] = acc;
+    p.ws_lse2[w] = real ? p.lse[r] * 1.44269504088896340736f : 0.f;
+  }
+}
+
+// Tile copies HBM -> LDS for the backward kernels: a tile of 64 rows of one
+// (batch, head) slab into the forward pass's row image (block pitch KBS) or
+// transposing image (block pitch VBS).  Copy j of wave w fills block w + NW·j.
+template <int D, int NW>
+struct BwdCopy {
+  using G = Geo<D>;
+  static constexpr int NCH = G::NCH, NBLK = G::NBLK, CPW = NBLK / NW;
+  static_assert(NBLK % NW == 0, "copy layout");
+  uint32_t lane_src, step;  // per-lane source offset within a tile, offset between a wave's copies
+  int wave;
+  __device__ __forceinline__ BwdCopy(int wave_, int lane) : wave(wave_) {
+    const int lrow = wave_ + NBLK * (lane / NCH), lchunk = 16 * (lane % NCH);
+    lane_src = (uint32_t)(lrow * D * 2 + lchunk);
+    step = (uint32_t)(NW * D * 2);
+  }
+  // rows [64·tile, 64·tile + 64) of a slab of `rows` rows; rows past the end read 0
+  template <int BS>
+  __device__ __forceinline__ void copy(const char* slab, int rows, int tile, unsigned char* dst) const {
+    const uint32_t off = (uint32_t)tile * 64u * D * 2u;
+    const uint32_t end = (uint32_t)rows * D * 2u;
+    const uint64_t base = (uint64_t)(uintptr_t)(slab + off);
+    const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xffffu)),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(end - off)), (uint32_t)kBufferFlags};
+    const uint32_t l0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_addr(dst) + BS * wave));
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) dma16(rs, l0 + BS * NW * j, lane_src + step * j);
+  }
+};
+
+// end of a step: own copies landed (vmcnt), then a bare barrier
+__device__ __forceinline__ void bwd_wait_join() {
+  __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// dQ: 8 waves x 32 query rows; loop over 64-key tiles
+// ---------------------------------------------------------------------------
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(BwdParams p) {
+  using G = Geo<D>;
+  constexpr int NW = 8, BR = 256, BC = 64, KB = 2, NB = D / 32, KS = D / 16;
+  constexpr int NBLK = G::NBLK, KBS = G::KBS, VBS = G::VBS, KT = G::KT, VT = G::VT;
+  // per stage: K row image, K transposing image, V row image
+  __shared__ __attribute__((aligned(16))) unsigned char kr0[KT], kr1[KT], kt0[VT], kt1[VT], vr0[KT], vr1[KT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int bid = blockIdx.x;
+  const int item = p.xcd_remap ? (bid & 7) * (p.num_wg >> 3) + (bid >> 3) : bid;
+  const int bh = __builtin_amdgcn_readfirstlane(item / p.n_qt);
+  const int qt_r = __builtin_amdgcn_readfirstlane(item - bh * p.n_qt);
+  const int qt = CAUSAL ? p.n_qt - 1 - qt_r : qt_r;  // causal: heaviest query tiles first
+  const int Lq = p.Lq, Lk = p.Lk;
+  const int i0 = qt * BR, i0w = i0 + 32 * wave;
+  const int off = CAUSAL ? p.kv_off : 0;
+
+  const char* const qslab = (const char*)p.q + (int64_t)bh * Lq * D * 2;
+  const char* const doslab = (const char*)p.dout + (int64_t)bh * Lq * D * 2;
+  const char* const kslab = (const char*)p.k + (int64_t)bh * Lk * D * 2;
+  const char* const vslab = (const char*)p.v + (int64_t)bh * Lk * D * 2;
+  const auto qrs = make_rsrc(qslab, (uint32_t)Lq * D * 2);
+  const auto dors = make_rsrc(doslab, (uint32_t)Lq * D * 2);
+
+  int n_kv = (Lk + BC - 1) / BC;
+  if constexpr (CAUSAL) n_kv = min(n_kv, (min(i0 + BR, Lq) - 1 + off) / BC + 1);
+
+  const BwdCopy<D, NW> cp(wave, lane);
+  auto copies = [&](int t, int st) {
+    cp.template copy<KBS>(kslab, Lk, t, st ? kr1 : kr0);
+    cp.template copy<VBS>(kslab, Lk, t, st ? kt1 : kt0);
+    cp.template copy<KBS>(vslab, Lk, t, st ? vr1 : vr0);
+  };
+  if (n_kv > 0) copies(0, 0);
+
+  // Q and dO rows of this lane as B operands (column = row l%32; slots of half g
+  // = head dims 16s+8g .. +7); the lane's LSE·log2(e) and Δ
+  const int qrow = i0w + l32;
+  u32x4 qr[KS], dr[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qr[s] = buf_load16(qrs, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2);
+    dr[s] = buf_load16(dors, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2);
+  }
+  const bool row_ok = qrow < Lq;
+  const float lse2 = row_ok ? p.ws_lse2[(int64_t)bh * p.Lq4 + qrow] : 0.f;
+  const float delta = row_ok ? p.ws_delta[(int64_t)bh * p.Lq4 + qrow] : 0.f;
+  const float c = p.c;
+
+  auto row_off = [](int rows, int BS) { return (rows % NBLK) * BS + (rows / NBLK) * 2 * D; };
+  const int k_off = (l32 % NBLK) * KBS + (l32 / NBLK) * 2 * D + 16 * g;
+  const int gi = lane >> 4, li = lane & 15;
+  const int t_off = (4 * (gi >> 1) + (li >> 2)) * VBS + 2 * (16 * (gi & 1) + 4 * (li & 3));
+
+  f32x16 dq[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) dq[nb] = f32x16{};
+
+  bwd_wait_join();
+  for (int t = 0; t < n_kv; ++t) {
+    const int st = t & 1;
+    if (t + 1 < n_kv) copies(t + 1, st ^ 1);
+    const int j0 = t * BC;
+    const bool active = !CAUSAL || j0 <= i0w + 31 + off;  // wave-uniform
+    if (active) {
+      const unsigned char* krb = st ? kr1 : kr0;
+      const unsigned char* ktb = st ? kt1 : kt0;
+      const unsigned char* vrb = st ? vr1 : vr0;
+      f32x16 S[KB], dP[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        S[kb] = f32x16{};
+        dP[kb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          S[kb] = mfma32<DT>(lds_read16(krb + k_off + row_off(32 * kb, KBS) + 32 * s), qr[s], S[kb]);
+          dP[kb] = mfma32<DT>(lds_read16(vrb + k_off + row_off(32 * kb, KBS) + 32 * s), dr[s], dP[kb]);
+        }
+      }
+      // key of S[kb][r] within the tile: 32kb + 8(r/4) + 4g + r%4; row = qrow
+      const bool need_mask = (CAUSAL && j0 + BC - 1 > i0w + off) || (j0 + BC > Lk);
+      const int lim_tail = Lk - j0 - 4 * g;
+      const int lim = CAUSAL ? min(qrow + off - j0 - 4 * g + 1, lim_tail) : lim_tail;
+      u32x4 db[KB][2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float ds[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int r = 8 * h + 2 * e + u;
+              float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -lse2));
+              if (need_mask) {
+                const int ko = 32 * kb + 8 * (r >> 2) + (r & 3);
+                pr = ko >= lim ? 0.f : pr;
+              }
+              ds[u] = pr * (dP[kb][r] - delta);
+            }
+            db[kb][h][e] = pack2<DT>(ds[0], ds[1]);
+          }
+      // dQᵀ += Kᵀ·dSᵀ: A = 8 keys of one head dim (two transposing reads)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const unsigned char* a0 = ktb + t_off + 64 * nb;
+            const u32x2 lo = lds_read_tr(a0 + row_off(32 * kb + 16 * h, VBS));
+            const u32x2 hi = lds_read_tr(a0 + row_off(32 * kb + 16 * h + 8, VBS));
+            dq[nb] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, db[kb][h], dq[nb]);
+          }
+    }
+    bwd_wait_join();
+  }
+
+  // epilogue: dQ = scale·dQᵀ; lane holds dims 32nb + 8(r/4) + 4g + r%4 of row qrow
+  const auto ors = make_rsrc((char*)p.dq + (int64_t)bh * Lq * D * 2, (uint32_t)Lq * D * 2);
+  const float sc = p.scale;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * nb + 8 * q4 + 4 * g;
+      const u32x2 w = {pack2<DT>(dq[nb][4 * q4] * sc, dq[nb][4 * q4 + 1] * sc),
+                       pack2<DT>(dq[nb][4 * q4 + 2] * sc, dq[nb][4 * q4 + 3] * sc)};
+      buf_store8(ors, (uint32_t)(qrow * D + d0) * 2, w);  // rows >= Lq are dropped
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: 4 waves x 32 keys; loop over 64-row query tiles
+// ---------------------------------------------------------------------------
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_dkdv_kernel(BwdParams p) {
+  using G = Geo<D>;
+  constexpr int NW = 4, BKV = 128, BQ = 64, QB = 2, NB = D / 32, KS = D / 16;
+  constexpr int NBLK = G::NBLK, KBS = G::KBS, VBS = G::VBS, KT = G::KT, VT = G::VT;
+  // per stage: Q row image, Q transposing image, dO row image, dO transposing image
+  __shared__ __attribute__((aligned(16))) unsigned char qr0[KT], qr1[KT], qt0[VT], qt1[VT];
+  __shared__ __attribute__((aligned(16))) unsigned char or0[KT], or1[KT], ot0[VT], ot1[VT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int bid = blockIdx.x;
+  const int item = p.xcd_remap ? (bid & 7) * (p.num_wg >> 3) + (bid >> 3) : bid;
+  const int bh = __builtin_amdgcn_readfirstlane(item / p.n_kt);
+  const int kt = __builtin_amdgcn_readfirstlane(item - bh * p.n_kt);  // causal: low tiles see most rows
+  const int Lq = p.Lq, Lk = p.Lk;
+  const int j0 = kt * BKV, j0w = j0 + 32 * wave;
+  const int off = CAUSAL ? p.kv_off : 0;
+
+  const char* const qslab = (const char*)p.q + (int64_t)bh * Lq * D * 2;
+  const char* const doslab = (const char*)p.dout + (int64_t)bh * Lq * D * 2;
+  const char* const kslab = (const char*)p.k + (int64_t)bh * Lk * D * 2;
+  const char* const vslab = (const char*)p.v + (int64_t)bh * Lk * D * 2;
+  const auto krs = make_rsrc(kslab, (uint32_t)Lk * D * 2);
+  const auto vrs = make_rsrc(vslab, (uint32_t)Lk * D * 2);
+  // (a head's rows start 16-byte aligned and groups of 4 rows lie wholly inside
+  // or wholly past the padded end, where they read 0)
+  const auto lrs = make_rsrc(p.ws_lse2 + (int64_t)bh * p.Lq4, (uint32_t)p.Lq4 * 4);
+  const auto drs = make_rsrc(p.ws_delta + (int64_t)bh * p.Lq4, (uint32_t)p.Lq4 * 4);
+
+  // query tiles that see any key of this workgroup: rows i >= j0 - off (causal)
+  const int n_q = (Lq + BQ - 1) / BQ;
+  const int t_b = CAUSAL ? max(0, j0 - off) / BQ : 0;
+
+  const BwdCopy<D, NW> cp(wave, lane);
+  auto copies = [&](int t, int st) {
+    cp.template copy<KBS>(qslab, Lq, t, st ? qr1 : qr0);
+    cp.template copy<VBS>(qslab, Lq, t, st ? qt1 : qt0);
+    cp.template copy<KBS>(doslab, Lq, t, st ? or1 : or0);
+    cp.template copy<VBS>(doslab, Lq, t, st ? ot1 : ot0);
+  };
+  if (t_b < n_q) copies(t_b, 0);
+
+  // K and V rows of this lane's key as B operands (column = key l%32; slots of
+  // half g = head dims 16s+8g .. +7); keys past Lk read 0
+  const int key = j0w + l32;
+  u32x4 kr[KS], vr[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kr[s] = buf_load16(krs, (uint32_t)(key * D + 16 * s + 8 * g) * 2);
+    vr[s] = buf_load16(vrs, (uint32_t)(key * D + 16 * s + 8 * g) * 2);
+  }
+  const float c = p.c;
+
+  auto row_off = [](int rows, int BS) { return (rows % NBLK) * BS + (rows / NBLK) * 2 * D; };
+  const int k_off = (l32 % NBLK) * KBS + (l32 / NBLK) * 2 * D + 16 * g;
+  const int gi = lane >> 4, li = lane & 15;
+  const int t_off = (4 * (gi >> 1) + (li >> 2)) * VBS + 2 * (16 * (gi & 1) + 4 * (li & 3));
+
+  f32x16 dv[NB], dk[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    dv[nb] = f32x16{};
+    dk[nb] = f32x16{};
+  }
+
+  bwd_wait_join();
+  for (int t = t_b; t < n_q; ++t) {
+    const int st = (t - t_b) & 1;
+    if (t + 1 < n_q) copies(t + 1, st ^ 1);
+    const int i0 = t * BQ;
+    // a wave whose keys no row of this tile sees skips it (wave-uniform)
+    const bool active = !CAUSAL || j0w <= i0 + BQ - 1 + off;
+    if (active) {
+      const unsigned char* qrb = st ? qr1 : qr0;
+      const unsigned char* qtb = st ? qt1 : qt0;
+      const unsigned char* orb = st ? or1 : or0;
+      const unsigned char* otb = st ? ot1 : ot0;
+      const bool need_mask = CAUSAL && j0w + 31 > i0 + off;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        // S = Q·Kᵀ and dP = dO·Vᵀ for 32 rows: lane holds key l%32 and rows
+        // 32qb + 8(r/4) + 4g + r%4 of the tile
+        f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          S = mfma32<DT>(lds_read16(qrb + k_off + row_off(32 * qb, KBS) + 32 * s), kr[s], S);
+          dP = mfma32<DT>(lds_read16(orb + k_off + row_off(32 * qb, KBS) + 32 * s), vr[s], dP);
+        }
+        // LSE·log2(e) and Δ of those rows: rows i0 + 32qb + 8a + 4g + 0..3
+        f32x4 ls[4], de[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const uint32_t ro = (uint32_t)(i0 + 32 * qb + 8 * a + 4 * g) * 4;
+          ls[a] = __builtin_bit_cast(f32x4, buf_load16(lrs, ro));
+          de[a] = __builtin_bit_cast(f32x4, buf_load16(drs, ro));
+        }
+        u32x4 pb[2], db[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pp[2], ds[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int r = 8 * h + 2 * e + u;
+              float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -ls[r >> 2][r & 3]));
+              if (need_mask) {
+                // key j0w + l32 visible to row i iff j <= i + off
+                const int row = i0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+                pr = key > row + off ? 0.f : pr;
+              }
+              pp[u] = pr;
+              ds[u] = pr * (dP[r] - de[r >> 2][r & 3]);
+            }
+            pb[h][e] = pack2<DT>(pp[0], pp[1]);
+            db[h][e] = pack2<DT>(ds[0], ds[1]);
+          }
+        // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS: A = 8 rows of one head dim (transposing reads)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const unsigned char* ao = otb + t_off + 64 * nb;
+            const u32x2 olo = lds_read_tr(ao + row_off(32 * qb + 16 * h, VBS));
+            const u32x2 ohi = lds_read_tr(ao + row_off(32 * qb + 16 * h + 8, VBS));
+            dv[nb] = mfma32<DT>(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pb[h], dv[nb]);
+            const unsigned char* aq = qtb + t_off + 64 * nb;
+            const u32x2 qlo = lds_read_tr(aq + row_off(32 * qb + 16 * h, VBS));
+            const u32x2 qhi = lds_read_tr(aq + row_off(32 * qb + 16 * h + 8, VBS));
+            dk[nb] = mfma32<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, db[h], dk[nb]);
+          }
+      }
+    }
+    bwd_wait_join();
+  }
+
+  // epilogue: lane holds dims 32nb + 8(r/4) + 4g + r%4 of key `key`
+  const auto dkrs = make_rsrc((char*)p.dk + (int64_t)bh * Lk * D * 2, (uint32_t)Lk * D * 2);
+  const auto dvrs = make_rsrc((char*)p.dv + (int64_t)bh * Lk * D * 2, (uint32_t)Lk * D * 2);
+  const float sc = p.scale;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * nb + 8 * q4 + 4 * g;
+      const u32x2 wk = {pack2<DT>(dk[nb][4 * q4] * sc, dk[nb][4 * q4 + 1] * sc),
+                        pack2<DT>(dk[nb][4 * q4 + 2] * sc, dk[nb][4 * q4 + 3] * sc)};
+      const u32x2 wv = {pack2<DT>(dv[nb][4 * q4], dv[nb][4 * q4 + 1]),
+                        pack2<DT>(dv[nb][4 * q4 + 2], dv[nb][4 * q4 + 3])};
+      buf_store8(dkrs, (uint32_t)(key * D + d0) * 2, wk);  // keys >= Lk are dropped
+      buf_store8(dvrs, (uint32_t)(key * D + d0) * 2, wv);
+    }
+}
+
+}  // namespace fa355
