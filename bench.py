@@ -4,6 +4,7 @@
     python bench.py --traffic-probe          # for rocprofv3 --pmc runs (see below)
     python bench.py --summarize-traffic DIR  # FETCH_SIZE/WRITE_SIZE CSVs -> profiles/*_traffic.md
     python bench.py --summarize-trace DIR    # kernel-trace stats CSV -> profiles/*_kernel_trace.md
+    python bench.py --pass bwd [--workload W] # the backward pass (fa_bwd) instead of the forward
 
 One step = one ``fa_fwd`` call (the whole hot path: one kernel) over the
 workload's seeded synthetic Q, K, V, which are resident in HBM before timing
@@ -11,7 +12,10 @@ starts.  The metric is attention-forward TFLOP/s with FLOP = 4·B·H·Lq·Lk·D,
 halved for causal, and its fraction of MI355X's dense bf16 MFMA peak.  The
 split-KV inference shapes (``--workload kvcache_16k`` and the like) step through
 ``fa_fwd_splitkv`` (main kernel plus merge); those below the ridge point report
-an HBM roofline instead.
+an HBM roofline instead.  ``--pass bwd`` times ``fa_bwd`` (row statistics, dQ,
+then dK/dV kernels) with o and lse from ``fa_fwd`` computed before timing and a
+seeded upstream gradient; its FLOP are 2.5x the forward's (five products of the
+same shape instead of two: the usual count for a recomputing backward pass).
 
 The shader clock of MI355X ramps over the first few hundred launches of this
 kernel, so the default warm-up is long (a few hundred milliseconds).
@@ -47,8 +51,9 @@ KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_06_amd", "csrc", f) for f 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_train7b_4k_traffic.md")
 
 
-def trace_file(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"fa_fwd_kernel_{workload}_kernel_trace.md")
+def trace_file(workload: str, pass_: str = "fwd") -> str:
+    kern = "fa_fwd_kernel" if pass_ == "fwd" else "fa_bwd_kernels"
+    return os.path.join(ROOT, "profiles", f"{kern}_{workload}_kernel_trace.md")
 
 COPY_BYTES = 1 << 30  # the plain device copy that calibrates the HBM byte counters
 
@@ -100,6 +105,49 @@ def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {len(heads)} heads of {w.name} (all {w.Lq} rows each), fp64 numpy, "
                       f"{dt:.1f} s wall, BLAS threads={threads}"}
+
+
+def cpu_baseline_bwd(inp, do, budget_s: float = 10.0) -> dict:
+    """The fp64 gradient oracle, unmodified, over whole heads of the workload until ~budget_s of CPU work."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_bwd_head_fp64
+
+    w = inp["workload"]
+    q, k, v = (inp[n].double().numpy() for n in ("q", "k", "v"))
+    d = do.double().numpy()
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        attention_bwd_head_fp64(q[b, h], k[b, h], v[b, h], d[b, h], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 2.5 * w.flops * done / len(heads)
+    threads = max([x.get("num_threads", 1) for x in threadpool_info() if x.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of {w.name} (dQ, dK, dV of every row), fp64 numpy, "
+                      f"{dt:.1f} s wall, BLAS threads={threads}"}
+
+
+def sampled_parity_bwd(inp, do, grads) -> dict:
+    """Two whole heads of dQ, dK, dV against the fp64 gradient oracle (the parity tests' bar)."""
+    import numpy as np
+
+    from oracle import attention_bwd_fp64
+
+    w = inp["workload"]
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, w.scale, w.causal, heads=heads)
+    tol = 2e-3 if w.dtype == "fp16" else 1e-2
+    worst = 0.0
+    for g, r in zip(grads, ref):
+        gc = g.double().cpu().numpy()
+        for b, h in heads:
+            worst = max(worst, float(np.abs(gc[b, h] - r[b, h]).max() / np.abs(r[b, h]).max()))
+    return {"heads_checked": len(heads), "max_err_over_max_ref": worst, "tol": tol, "pass": bool(worst <= tol)}
 
 
 def sampled_parity(inp, o, lse, n_rows: int = 128) -> dict:
@@ -209,20 +257,26 @@ def summarize_traffic(directory: str, w) -> str:
     return "\n".join(lines)
 
 
-def summarize_trace(directory: str, w, bench_line: str | None) -> str:
+def summarize_trace(directory: str, w, bench_line: str | None, pass_: str = "fwd") -> str:
     rows = _csv_rows(directory, "*kernel_stats.csv")
     if not rows:
         raise SystemExit("no kernel_stats.csv under " + directory)
-    keep = [r for r in rows if "fa_fwd_kernel" in r.get("Name", "") or "fa_merge_kernel" in r.get("Name", "")]
+    keep = [r for r in rows if "fa_" in r.get("Name", "") and "fa355" in r.get("Name", "")]
     hdr = list(rows[0].keys())
     wl = "" if w.name == "train7b_4k" else f" --workload {w.name}"
+    if pass_ == "bwd":
+        wl += " --pass bwd"
+    what = "fa_fwd_kernel" if pass_ == "fwd" else "the fa_bwd kernels"
     lines = [
-        f"# rocprofv3 kernel trace: fa_fwd_kernel on {w.name} ({w.description})",
+        f"# rocprofv3 kernel trace: {what} on {w.name} ({w.description})",
         "",
         "Command (from the repository root on the GPU box):",
         "",
         f"    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o t -- python3 bench.py{wl} --no-cpu-baseline --no-parity",
         f"    python3 bench.py{wl} --summarize-trace gpurun_out/trace --bench-log <that run's stdout>",
+        "",
+        "(fa_fwd_kernel rows in a backward trace are the one forward call that makes o and lse.)" if pass_ == "bwd"
+        else "",
         "",
         "kernel_stats.csv rows for the kernel (durations in ns):",
         "",
@@ -236,6 +290,77 @@ def summarize_trace(directory: str, w, bench_line: str | None) -> str:
     return "\n".join(lines)
 
 
+def bench_bwd(args, w) -> int:
+    import torch
+
+    import attn_inputs
+    import tiled_attention_06_amd as fa
+
+    log(f"bench bwd: {w.description}; generating inputs (seed {w.seed}, dO seed {w.seed + 100})")
+    inp = attn_inputs.make_inputs(w)
+    do_cpu = attn_inputs.make_dout((w.B, w.H, w.Lq, w.D), w.dtype, seed=w.seed + 100)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    do = do_cpu.to(dev)
+    o, lse = fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.Lq), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, causal=w.causal, scale=w.scale, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    flops = 2.5 * w.flops
+    step_ms = [s.elapsed_time(e) for s, e in ev]
+    mean_s = sum(step_ms) / len(step_ms) / 1e3
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / mean_s / 1e12
+    log(f"bench bwd: {args.steps} steps in {wall * 1e3:.2f} ms; step mean {mean_s * 1e6:.1f} us; "
+        f"{achieved:.1f} TFLOP/s = {100 * achieved / PEAK_BF16_TFLOPS:.2f}% of peak")
+    out = {
+        "metric": f"attention bwd TFLOP/s ({w.description})",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "bwd", "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "D": w.D,
+                   "causal": w.causal, "scale": w.scale, "seed": w.seed, "dout_seed": w.seed + 100,
+                   "flop_per_step": flops},
+        "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 5), "traffic": None,
+                     "kernel": "fa_bwd_prep_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (the events bracket all "
+                               "three)", "mean_launch_us": round(mean_s * 1e6, 3)},
+    }
+    if not args.no_parity:
+        out["parity"] = sampled_parity_bwd(inp, do_cpu, (dq, dk, dv))
+        log(f"bench bwd: parity {out['parity']}")
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_bwd(inp, do_cpu)
+        log(f"bench bwd: cpu baseline {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +368,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="train7b_4k",
                     help="a name from attn_inputs.WORKLOADS or attn_inputs.SPLIT_WORKLOADS")
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd",
+                    help="fwd: fa_fwd (the default line); bwd: fa_bwd")
     ap.add_argument("--splits", type=int, default=None,
                     help="key splits (fa_fwd_splitkv when > 1); default: the workload's own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -273,8 +400,8 @@ def main() -> int:
         if args.bench_log and os.path.exists(args.bench_log):
             with open(args.bench_log, encoding="utf-8") as f:
                 line = next((x for x in f if x.startswith("{")), None)
-        text = summarize_trace(args.summarize_trace, w, line)
-        with open(trace_file(w.name), "w", encoding="utf-8") as f:
+        text = summarize_trace(args.summarize_trace, w, line, args.pass_)
+        with open(trace_file(w.name, args.pass_), "w", encoding="utf-8") as f:
             f.write(text)
         print(text)
         return 0
@@ -286,6 +413,8 @@ def main() -> int:
     if args.traffic_probe:
         traffic_probe(w, steps=3)
         return 0
+    if args.pass_ == "bwd":
+        return bench_bwd(args, w)
     log(f"bench: {w.description}; generating inputs (seed {w.seed})")
     inp = attn_inputs.make_inputs(w)
     dev = torch.device("cuda:0")

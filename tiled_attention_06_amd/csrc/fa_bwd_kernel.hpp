@@ -295,6 +295,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // per stage: Q row image, Q transposing image, dO row image, dO transposing image
   __shared__ __attribute__((aligned(16))) unsigned char qr0[KT], qr1[KT], qt0[VT], qt1[VT];
   __shared__ __attribute__((aligned(16))) unsigned char or0[KT], or1[KT], ot0[VT], ot1[VT];
+  // per stage: LSE·log2(e) and Δ of the tile's 64 rows (a 1 KB copy each; the
+  // first 256 bytes are used)
+  __shared__ __attribute__((aligned(16))) float ls0[256], ls1[256], de0[256], de1[256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -315,21 +318,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const char* const vslab = (const char*)p.v + (int64_t)bh * Lk * D * 2;
   const auto krs = make_rsrc(kslab, (uint32_t)Lk * D * 2);
   const auto vrs = make_rsrc(vslab, (uint32_t)Lk * D * 2);
-  // (a head's rows start 16-byte aligned and groups of 4 rows lie wholly inside
-  // or wholly past the padded end, where they read 0)
-  const auto lrs = make_rsrc(p.ws_lse2 + (int64_t)bh * p.Lq4, (uint32_t)p.Lq4 * 4);
-  const auto drs = make_rsrc(p.ws_delta + (int64_t)bh * p.Lq4, (uint32_t)p.Lq4 * 4);
 
   // query tiles that see any key of this workgroup: rows i >= j0 - off (causal)
   const int n_q = (Lq + BQ - 1) / BQ;
   const int t_b = CAUSAL ? max(0, j0 - off) / BQ : 0;
 
   const BwdCopy<D, NW> cp(wave, lane);
+  // row statistics of tile t: rows past the padded end read 0
+  auto copy_stats = [&](const float* base, int t, float* dst) {
+    const uint64_t a = (uint64_t)(uintptr_t)(base + (int64_t)bh * p.Lq4 + (int64_t)t * BQ);
+    const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p.Lq4 - t * BQ) * 4u)),
+                      (uint32_t)kBufferFlags};
+    dma16(rs, (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(dst)), (uint32_t)(16 * lane));
+  };
   auto copies = [&](int t, int st) {
     cp.template copy<KBS>(qslab, Lq, t, st ? qr1 : qr0);
     cp.template copy<VBS>(qslab, Lq, t, st ? qt1 : qt0);
     cp.template copy<KBS>(doslab, Lq, t, st ? or1 : or0);
     cp.template copy<VBS>(doslab, Lq, t, st ? ot1 : ot0);
+    if (wave == 0) copy_stats(p.ws_lse2, t, st ? ls1 : ls0);
+    if (wave == 1) copy_stats(p.ws_delta, t, st ? de1 : de0);
   };
   if (t_b < n_q) copies(t_b, 0);
 
@@ -356,6 +366,88 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     dk[nb] = f32x16{};
   }
 
+  // One 64-row query tile.  In S and dP the lane holds key l%32 and rows
+  // 32qb + 8(r/4) + 4g + r%4 of the tile.  Half qb: S = Q·Kᵀ and dP = dO·Vᵀ, the
+  // weights and dS in registers, then dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS.
+  auto products = [&](int qb, const unsigned char* qrb, const unsigned char* orb, f32x16& S, f32x16& dP) {
+    S = f32x16{};
+    dP = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      S = mfma32<DT>(lds_read16(qrb + k_off + row_off(32 * qb, KBS) + 32 * s), kr[s], S);
+      dP = mfma32<DT>(lds_read16(orb + k_off + row_off(32 * qb, KBS) + 32 * s), vr[s], dP);
+    }
+  };
+  auto grads = [&](auto MASK, int qb, int i0, const f32x16& S, const f32x16& dP, const unsigned char* qtb,
+                   const unsigned char* otb, const float* lsb, const float* deb) {
+    // LSE·log2(e) and Δ of the lane's rows: tile rows 32qb + 8a + 4g + 0..3
+    f32x4 ls[4], de[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      ls[a] = *(const f32x4*)(lsb + 32 * qb + 8 * a + 4 * g);
+      de[a] = *(const f32x4*)(deb + 32 * qb + 8 * a + 4 * g);
+    }
+    u32x4 pb[2], db[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pp[2], ds[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 8 * h + 2 * e + u;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -ls[r >> 2][r & 3]));
+          if constexpr (decltype(MASK)::value) {
+            // key j0w + l32 visible to row i iff j <= i + off
+            const int row = i0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+            pr = key > row + off ? 0.f : pr;
+          }
+          pp[u] = pr;
+          ds[u] = pr * (dP[r] - de[r >> 2][r & 3]);
+        }
+        pb[h][e] = pack2<DT>(pp[0], pp[1]);
+        db[h][e] = pack2<DT>(ds[0], ds[1]);
+      }
+    // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS: A = 8 rows of one head dim (transposing reads)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const unsigned char* ao = otb + t_off + 64 * nb;
+        const u32x2 olo = lds_read_tr(ao + row_off(32 * qb + 16 * h, VBS));
+        const u32x2 ohi = lds_read_tr(ao + row_off(32 * qb + 16 * h + 8, VBS));
+        dv[nb] = mfma32<DT>(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pb[h], dv[nb]);
+        const unsigned char* aq = qtb + t_off + 64 * nb;
+        const u32x2 qlo = lds_read_tr(aq + row_off(32 * qb + 16 * h, VBS));
+        const u32x2 qhi = lds_read_tr(aq + row_off(32 * qb + 16 * h + 8, VBS));
+        dk[nb] = mfma32<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, db[h], dk[nb]);
+      }
+  };
+  // D = 64, full tiles: the products of both halves first (four independent MFMA
+  // chains), so that the MFMAs of one half can overlap the VALU work of the other
+  // (measured faster at D = 64, slower at D = 128).  Otherwise one half after the
+  // other (fewer live registers).
+  auto tile_body = [&](auto MASK, int i0, const unsigned char* qrb, const unsigned char* qtb,
+                       const unsigned char* orb, const unsigned char* otb, const float* lsb, const float* deb) {
+    if constexpr (decltype(MASK)::value || D == 128) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x16 S, dP;
+        products(qb, qrb, orb, S, dP);
+        grads(MASK, qb, i0, S, dP, qtb, otb, lsb, deb);
+        // (a scheduling barrier per half: operand reads of the next half are not
+        // hoisted over this one, which would run out of registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      f32x16 S0, dP0, S1, dP1;
+      products(0, qrb, orb, S0, dP0);
+      products(1, qrb, orb, S1, dP1);
+      grads(MASK, 0, i0, S0, dP0, qtb, otb, lsb, deb);
+      grads(MASK, 1, i0, S1, dP1, qtb, otb, lsb, deb);
+    }
+  };
+
   bwd_wait_join();
   for (int t = t_b; t < n_q; ++t) {
     const int st = (t - t_b) & 1;
@@ -368,61 +460,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const unsigned char* qtb = st ? qt1 : qt0;
       const unsigned char* orb = st ? or1 : or0;
       const unsigned char* otb = st ? ot1 : ot0;
-      const bool need_mask = CAUSAL && j0w + 31 > i0 + off;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        // S = Q·Kᵀ and dP = dO·Vᵀ for 32 rows: lane holds key l%32 and rows
-        // 32qb + 8(r/4) + 4g + r%4 of the tile
-        f32x16 S = f32x16{}, dP = f32x16{};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          S = mfma32<DT>(lds_read16(qrb + k_off + row_off(32 * qb, KBS) + 32 * s), kr[s], S);
-          dP = mfma32<DT>(lds_read16(orb + k_off + row_off(32 * qb, KBS) + 32 * s), vr[s], dP);
-        }
-        // LSE·log2(e) and Δ of those rows: rows i0 + 32qb + 8a + 4g + 0..3
-        f32x4 ls[4], de[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const uint32_t ro = (uint32_t)(i0 + 32 * qb + 8 * a + 4 * g) * 4;
-          ls[a] = __builtin_bit_cast(f32x4, buf_load16(lrs, ro));
-          de[a] = __builtin_bit_cast(f32x4, buf_load16(drs, ro));
-        }
-        u32x4 pb[2], db[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pp[2], ds[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int r = 8 * h + 2 * e + u;
-              float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -ls[r >> 2][r & 3]));
-              if (need_mask) {
-                // key j0w + l32 visible to row i iff j <= i + off
-                const int row = i0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-                pr = key > row + off ? 0.f : pr;
-              }
-              pp[u] = pr;
-              ds[u] = pr * (dP[r] - de[r >> 2][r & 3]);
-            }
-            pb[h][e] = pack2<DT>(pp[0], pp[1]);
-            db[h][e] = pack2<DT>(ds[0], ds[1]);
-          }
-        // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS: A = 8 rows of one head dim (transposing reads)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const unsigned char* ao = otb + t_off + 64 * nb;
-            const u32x2 olo = lds_read_tr(ao + row_off(32 * qb + 16 * h, VBS));
-            const u32x2 ohi = lds_read_tr(ao + row_off(32 * qb + 16 * h + 8, VBS));
-            dv[nb] = mfma32<DT>(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pb[h], dv[nb]);
-            const unsigned char* aq = qtb + t_off + 64 * nb;
-            const u32x2 qlo = lds_read_tr(aq + row_off(32 * qb + 16 * h, VBS));
-            const u32x2 qhi = lds_read_tr(aq + row_off(32 * qb + 16 * h + 8, VBS));
-            dk[nb] = mfma32<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, db[h], dk[nb]);
-          }
-      }
+      const float* lsb = st ? ls1 : ls0;
+      const float* deb = st ? de1 : de0;
+      // causal: every tile takes the masked body (one compare and select per
+      // element; a second, unmasked copy of the body for tiles below the diagonal
+      // made the compiler spill)
+      if constexpr (CAUSAL)
+        tile_body(std::true_type{}, i0, qrb, qtb, orb, otb, lsb, deb);
+      else
+        tile_body(std::false_type{}, i0, qrb, qtb, orb, otb, lsb, deb);
     }
     bwd_wait_join();
   }
