@@ -266,13 +266,18 @@ def summarize_trace(directory: str, w, bench_line: str | None, pass_: str = "fwd
     wl = "" if w.name == "train7b_4k" else f" --workload {w.name}"
     if pass_ == "bwd":
         wl += " --pass bwd"
+    run_args = wl
+    if bench_line:
+        j = json.loads(bench_line)
+        if (j.get("steps"), j.get("warmup")) != (200, 500):
+            run_args += f" --steps {j['steps']} --warmup {j['warmup']}"
     what = "fa_fwd_kernel" if pass_ == "fwd" else "the fa_bwd kernels"
     lines = [
         f"# rocprofv3 kernel trace: {what} on {w.name} ({w.description})",
         "",
         "Command (from the repository root on the GPU box):",
         "",
-        f"    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o t -- python3 bench.py{wl} --no-cpu-baseline --no-parity",
+        f"    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o t -- python3 bench.py{run_args} --no-cpu-baseline --no-parity",
         f"    python3 bench.py{wl} --summarize-trace gpurun_out/trace --bench-log <that run's stdout>",
         "",
         "(fa_fwd_kernel rows in a backward trace are the one forward call that makes o and lse.)" if pass_ == "bwd"
