@@ -47,6 +47,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .philox import dropout_keep, keep_threshold
+
 __all__ = ["attention_fp64", "attention_head_fp64"]
 
 
@@ -60,12 +62,15 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def attention_head_fp64(q, k, v, scale: float, causal: bool, rows=None, chunk: int = 1024):
+def attention_head_fp64(q, k, v, scale: float, causal: bool, rows=None, chunk: int = 1024,
+                        dropout_p: float = 0.0, seed: int = 0, bh: int = 0):
     """One head.  q: [Lq, D], k/v: [Lk, D] (fp64).  Returns (O [R, D], LSE [R]) fp64.
 
     ``rows`` selects which query rows to evaluate (default: all, in order); each
     row is computed from its own definition, so a subset gives the same values
-    as the full computation restricted to it.
+    as the full computation restricted to it.  ``dropout_p`` > 0 applies dropout
+    to the normalised weights with the keep-mask of ``oracle/philox.py`` for
+    (``bh``, row, key) and ``seed``; LSE is that of the weights before dropout.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -93,13 +98,17 @@ def attention_head_fp64(q, k, v, scale: float, causal: bool, rows=None, chunk: i
         m = S.max(axis=1)
         P = np.exp(S - m[:, None])
         l = P.sum(axis=1)
+        if dropout_p:
+            # [DF §4.1] dropout on the weights: kept ones scaled by 256/T (reading in philox.py)
+            P = P * dropout_keep(bh, r, np.arange(Lk), dropout_p, seed) * (256.0 / keep_threshold(dropout_p))
         # stage 3: product with V, normalised once per row ([DF §2.1] stage 3, [DF §2.2])
         O[c0 : c0 + chunk] = (P @ v) / l[:, None]
         LSE[c0 : c0 + chunk] = m + np.log(l)
     return O, LSE
 
 
-def attention_fp64(q, k, v, scale: float, causal: bool, rows=None, heads=None, chunk: int = 1024):
+def attention_fp64(q, k, v, scale: float, causal: bool, rows=None, heads=None, chunk: int = 1024,
+                   dropout_p: float = 0.0, seed: int = 0):
     """Batched attention.  q: [B,H,Lq,D], k/v: [B,H,Lk,D] (numpy or CPU torch, any float dtype).
 
     Returns (O, LSE) as fp64 numpy arrays of shapes [B,H,R,D] and [B,H,R], where R
@@ -117,5 +126,6 @@ def attention_fp64(q, k, v, scale: float, causal: bool, rows=None, heads=None, c
     LSE = np.full((B, H, R), np.nan)
     pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     for b, h in pairs:
-        O[b, h], LSE[b, h] = attention_head_fp64(q[b, h], k[b, h], v[b, h], scale, causal, rows, chunk)
+        O[b, h], LSE[b, h] = attention_head_fp64(q[b, h], k[b, h], v[b, h], scale, causal, rows, chunk,
+                                                 dropout_p, seed, b * H + h)
     return O, LSE

@@ -40,6 +40,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .philox import dropout_keep, keep_threshold
+
 __all__ = ["attention_bwd_fp64", "attention_bwd_head_fp64"]
 
 
@@ -53,8 +55,12 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def attention_bwd_head_fp64(q, k, v, do, scale: float, causal: bool, chunk: int = 1024):
-    """One head.  q, do: [Lq, D]; k, v: [Lk, D] (fp64).  Returns (dQ [Lq,D], dK [Lk,D], dV [Lk,D])."""
+def attention_bwd_head_fp64(q, k, v, do, scale: float, causal: bool, chunk: int = 1024, dropout_p: float = 0.0,
+                            seed: int = 0, bh: int = 0):
+    """One head.  q, do: [Lq, D]; k, v: [Lk, D] (fp64).  Returns (dQ [Lq,D], dK [Lk,D], dV [Lk,D]).
+
+    With ``dropout_p`` > 0 the forward output is O = (P ∘ M) V, M = keep·256/T the
+    dropout factors of ``oracle/philox.py`` for (``bh``, row, key) and ``seed``."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     Lq, D = q.shape
     Lk = k.shape[0]
@@ -74,9 +80,16 @@ def attention_bwd_head_fp64(q, k, v, do, scale: float, causal: bool, chunk: int 
             S[np.arange(Lk)[None, :] > r[:, None] + off] = -np.inf
         E = np.exp(S - S.max(axis=1, keepdims=True))
         P = E / E.sum(axis=1, keepdims=True)
-        # O = P V: gradient to V, and to P
-        dV += P.T @ do[r]
+        # dropout factors M (all ones without dropout): O = (P ∘ M) V
+        M = None
+        if dropout_p:
+            M = dropout_keep(bh, r, np.arange(Lk), dropout_p, seed) * (256.0 / keep_threshold(dropout_p))
+        Pd = P if M is None else P * M
+        # gradient to V, and to P through the dropout factors
+        dV += Pd.T @ do[r]
         dP = do[r] @ v.T
+        if M is not None:
+            dP = dP * M
         # row-wise softmax Jacobian: dS = P * (dP - <P, dP>_row)
         dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
         # s = scale * q . k: gradients to q and k
@@ -85,7 +98,8 @@ def attention_bwd_head_fp64(q, k, v, do, scale: float, causal: bool, chunk: int 
     return dQ, dK, dV
 
 
-def attention_bwd_fp64(q, k, v, do, scale: float, causal: bool, heads=None, chunk: int = 1024):
+def attention_bwd_fp64(q, k, v, do, scale: float, causal: bool, heads=None, chunk: int = 1024,
+                       dropout_p: float = 0.0, seed: int = 0):
     """Batched gradients.  q, do: [B,H,Lq,D]; k, v: [B,H,Lk,D] (numpy or CPU torch, any float dtype).
 
     Returns (dQ, dK, dV) as fp64 numpy arrays of the inputs' shapes.  ``heads``
@@ -104,5 +118,5 @@ def attention_bwd_fp64(q, k, v, do, scale: float, causal: bool, heads=None, chun
     pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     for b, h in pairs:
         dQ[b, h], dK[b, h], dV[b, h] = attention_bwd_head_fp64(q[b, h], k[b, h], v[b, h], do[b, h], scale,
-                                                               causal, chunk)
+                                                               causal, chunk, dropout_p, seed, b * H + h)
     return dQ, dK, dV

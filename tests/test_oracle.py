@@ -338,8 +338,9 @@ def _load_mutant(name):
         src = f.read()
     assert old in src, f"mutation anchor for {name} not found in the oracle"
     src = src.replace(old, new, 1)
-    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod = types.ModuleType(f"oracle.oracle_mutant_{name}")
     mod.__dict__["__name__"] = mod.__name__
+    mod.__dict__["__package__"] = "oracle"  # the oracle's relative imports resolve in its package
     sys.modules[mod.__name__] = mod
     exec(compile(src, ORACLE_SRC + f"<{name}>", "exec"), mod.__dict__)
     return mod

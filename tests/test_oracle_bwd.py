@@ -70,6 +70,32 @@ def pin_finite_differences(grad):
                                        err_msg=f"d{name}, shape {(Lq, Lk, D)}, causal={causal}")
 
 
+def pin_finite_differences_dropout(grad):
+    """With dropout (a fixed keep-mask for a given seed), central differences of the forward
+    oracle agree with the gradients, every element of q, k and v."""
+    h = 1e-5
+    for n, (Lq, Lk, D, causal) in enumerate([(7, 7, 3, False), (5, 9, 2, True)]):
+        q, k, v, do = _inputs(150 + n, 1, 2, Lq, Lk, D)
+        scale, p, seed = 0.6, 0.3, 1234 + n
+
+        def f(q_, k_, v_):
+            O, _ = attention_fp64(q_, k_, v_, scale, causal, dropout_p=p, seed=seed)
+            return float((O * do).sum())
+
+        dQ, dK, dV = grad(q, k, v, do, scale, causal, dropout_p=p, seed=seed)
+        for name, x, g in (("q", q, dQ), ("k", k, dK), ("v", v, dV)):
+            num = np.empty_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                num[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+            np.testing.assert_allclose(g, num, rtol=0, atol=1e-7,
+                                       err_msg=f"dropout d{name}, shape {(Lq, Lk, D)}, causal={causal}")
+
+
 def pin_autograd(grad):
     """torch autograd through scaled_dot_product_attention on the CPU in float64 (with an explicit
     boolean mask for the bottom-right causal rule) gives the same gradients to 1e-12."""
@@ -149,13 +175,13 @@ def pin_zero_upstream(grad):
         assert np.all(g == 0)
 
 
-PINS = [pin_finite_differences, pin_autograd, pin_sum_rules, pin_equal_keys, pin_closed_form,
-        pin_causal_edges, pin_zero_upstream]
+PINS = [pin_finite_differences, pin_finite_differences_dropout, pin_autograd, pin_sum_rules, pin_equal_keys,
+        pin_closed_form, pin_causal_edges, pin_zero_upstream]
 
 
-def _oracle_grad(q, k, v, do, scale, causal):
+def _oracle_grad(q, k, v, do, scale, causal, **kw):
     # rows in chunks of 4, so the pins also cover the accumulation of dK and dV over chunks
-    return attention_bwd_fp64(q, k, v, do, scale, causal, chunk=4)
+    return attention_bwd_fp64(q, k, v, do, scale, causal, chunk=4, **kw)
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -177,13 +203,16 @@ MUTANTS = {
     "dq_from_values": ("dQ[r] = scale * (dS @ k)", "dQ[r] = scale * (dS @ v)"),
     "dk_from_upstream": ("dK += scale * (dS.T @ q[r])", "dK += scale * (dS.T @ do[r])"),
     "dp_from_keys": ("dP = do[r] @ v.T", "dP = do[r] @ k.T"),
-    "dv_unnormalised": ("dV += P.T @ do[r]", "dV += E.T @ do[r]"),
+    "dv_unnormalised": ("dV += Pd.T @ do[r]", "dV += E.T @ do[r]"),
     "softmax_unnormalised": ("P = E / E.sum(axis=1, keepdims=True)", "P = E"),
     "no_causal_mask": ("S[np.arange(Lk)[None, :] > r[:, None] + off] = -np.inf", "pass"),
     "mask_top_left": ("> r[:, None] + off] = -np.inf", "> r[:, None]] = -np.inf"),
     "mask_excludes_diagonal": ("> r[:, None] + off] = -np.inf", ">= r[:, None] + off] = -np.inf"),
     "dk_overwritten_per_chunk": ("dK += scale * (dS.T @ q[r])", "dK = scale * (dS.T @ q[r])"),
-    "dv_overwritten_per_chunk": ("dV += P.T @ do[r]", "dV = P.T @ do[r]"),
+    "dv_overwritten_per_chunk": ("dV += Pd.T @ do[r]", "dV = Pd.T @ do[r]"),
+    "dropout_missing_in_dp": ("            dP = dP * M", "            pass"),
+    "dropout_missing_in_dv": ("Pd = P if M is None else P * M", "Pd = P"),
+    "dropout_unscaled": ("* (256.0 / keep_threshold(dropout_p))", ""),
     "scale_missing_in_scores": ("S = (q[r] @ k.T) * scale", "S = q[r] @ k.T"),
 }
 
@@ -194,8 +223,9 @@ def _load_mutant(name):
         src = f.read()
     assert old in src, f"mutation anchor for {name} not found in the oracle"
     src = src.replace(old, new, 1)
-    mod = types.ModuleType(f"oracle_bwd_mutant_{name}")
+    mod = types.ModuleType(f"oracle.oracle_bwd_mutant_{name}")
     mod.__dict__["__name__"] = mod.__name__
+    mod.__dict__["__package__"] = "oracle"  # the oracle's relative imports resolve in its package
     sys.modules[mod.__name__] = mod
     exec(compile(src, ORACLE_SRC + f"<{name}>", "exec"), mod.__dict__)
     return mod
@@ -205,8 +235,8 @@ def _load_mutant(name):
 def test_planted_mistake_is_caught(name):
     mod = _load_mutant(name)
 
-    def grad(q, k, v, do, scale, causal):
-        return mod.attention_bwd_fp64(q, k, v, do, scale, causal, chunk=4)
+    def grad(q, k, v, do, scale, causal, **kw):
+        return mod.attention_bwd_fp64(q, k, v, do, scale, causal, chunk=4, **kw)
 
     failures = []
     for pin in PINS:

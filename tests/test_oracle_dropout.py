@@ -1,0 +1,210 @@
+"""Pins for the dropout parts of the oracle: the Philox4x32-10 stream, the keep-mask and
+dropped-out attention (oracle/philox.py, oracle/attention.py).
+
+Pages cited:
+  [DF] "FlashAttention数据流优化：MI50显存与带宽瓶颈实战"  (kwkr.cn/news/544806)
+
+[DF §4.1] takes a dropout probability and specifies no generator; the reading
+(Philox4x32-10, a 4 x 4 block of (row, key) per counter, byte < T keeps) is in
+oracle/philox.py.  What the mathematics fixes and is pinned here: the Weyl
+constants of the key schedule against their closed forms, the statistics of the
+bytes and of the keep-mask, p = 0 giving attention without dropout exactly, LSE
+unaffected, the dropped-out output equal to its definition through the
+(separately pinned) forward oracle's LSE, and unbiasedness over seeds.  The
+generator's outputs are not pinned against published test vectors (none on the
+pages): bit-identity with other Philox4x32-10 implementations is parity unpinned.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+
+from oracle import attention_fp64
+from oracle import philox
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ATTN_SRC = os.path.join(os.path.dirname(HERE), "oracle", "attention.py")
+
+
+def test_weyl_constants_closed_forms():
+    phi = (1 + math.sqrt(5)) / 2
+    assert philox.W0 == math.floor(2 ** 32 / phi)
+    assert philox.W1 == math.floor(2 ** 32 * (math.sqrt(3) - 1))
+
+
+def test_round_is_a_bijection_on_counters():
+    # each round is invertible (odd multipliers), so distinct counters give distinct outputs
+    assert int(philox.M0) % 2 == 1 and int(philox.M1) % 2 == 1
+    n = 1 << 18
+    c = np.arange(n, dtype=np.uint64)
+    w = philox.philox4x32_10(c & 0xFFFF, c >> 16, np.zeros(n), np.zeros(n), 7, 9)
+    packed = {(int(a), int(b), int(x), int(y)) for a, b, x, y in zip(*w)}
+    assert len(packed) == n
+
+
+def test_byte_statistics():
+    n = 1 << 16
+    c = np.arange(n, dtype=np.uint64)
+    words = np.stack(philox.philox4x32_10(c, np.full(n, 3), np.full(n, 5), np.zeros(n), 0x1234, 0xABCD))
+    b = np.concatenate([(words >> np.uint32(8 * s)) & np.uint32(0xFF) for s in range(4)]).ravel()
+    counts = np.bincount(b, minlength=256)
+    exp = b.size / 256
+    chi2 = float(((counts - exp) ** 2 / exp).sum())
+    assert 255 - 5 * math.sqrt(2 * 255) < chi2 < 255 + 5 * math.sqrt(2 * 255), chi2
+    # adjacent counters: correlation of the first word's bytes is near zero
+    x = (words[0] & np.uint32(0xFF)).astype(np.float64)
+    r = np.corrcoef(x[:-1], x[1:])[0, 1]
+    assert abs(r) < 5 / math.sqrt(n), r
+    # every output bit is set about half of the time
+    bits = ((words[:, :, None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)).mean(axis=1)
+    assert np.abs(bits - 0.5).max() < 5 * 0.5 / math.sqrt(n)
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
+def test_keep_fraction(p):
+    T = philox.keep_threshold(p)
+    keep = philox.dropout_keep(3, np.arange(512), np.arange(512), p, seed=2024)
+    f, n = keep.mean(), keep.size
+    kp = T / 256
+    assert abs(f - kp) < 5 * math.sqrt(kp * (1 - kp) / n)
+
+
+def test_keep_threshold_reading():
+    assert philox.keep_threshold(0.0) == 256 and philox.keep_threshold(0.1) == 230
+    assert philox.keep_threshold(0.5) == 128 and philox.keep_threshold(0.998) == 1
+    for bad in (-0.1, 1.0, 0.999, float("nan")):
+        with pytest.raises(ValueError):
+            philox.keep_threshold(bad)
+
+
+def test_mask_depends_on_seed_head_and_position_only():
+    a = philox.dropout_keep(5, np.arange(40), np.arange(50), 0.5, seed=99)
+    sub = philox.dropout_keep(5, np.arange(13, 31), np.arange(7, 44), 0.5, seed=99)
+    assert np.array_equal(a[13:31, 7:44], sub)
+    assert not np.array_equal(a, philox.dropout_keep(6, np.arange(40), np.arange(50), 0.5, seed=99))
+    assert not np.array_equal(a, philox.dropout_keep(5, np.arange(40), np.arange(50), 0.5, seed=98))
+    assert not np.array_equal(a, philox.dropout_keep(5, np.arange(40), np.arange(50), 0.5, seed=99 + (1 << 32)))
+
+
+# --------------------------------------------------------------------------------------------
+# dropped-out attention
+# --------------------------------------------------------------------------------------------
+
+def _qkv(seed, B=1, H=2, Lq=9, Lk=11, D=4):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((B, H, Lq, D)), r.standard_normal((B, H, Lk, D)), r.standard_normal((B, H, Lk, D)))
+
+
+def pin_zero_probability(attn):
+    q, k, v = _qkv(1)
+    for causal in (False, True):
+        O0, L0 = attention_fp64(q, k, v, 0.5, causal)
+        O1, L1 = attn(q, k, v, 0.5, causal, 0.0, 77)
+        np.testing.assert_allclose(O1, O0, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(L1, L0, rtol=0, atol=1e-13)
+
+
+def pin_lse_unaffected(attn):
+    q, k, v = _qkv(2)
+    _, L0 = attention_fp64(q, k, v, 0.5, True)
+    _, L1 = attn(q, k, v, 0.5, True, 0.4, 5)
+    np.testing.assert_allclose(L1, L0, rtol=0, atol=1e-13)
+
+
+def pin_definition_through_lse(attn):
+    """O_i = (256/T) Σ_j exp(s_ij − LSE_i) keep_ij v_j with LSE from the dropout-free oracle."""
+    q, k, v = _qkv(3, B=2, H=2, Lq=6, Lk=10)
+    p, seed, scale = 0.35, 4242, 0.45
+    T = philox.keep_threshold(p)
+    for causal in (False, True):
+        O, _ = attn(q, k, v, scale, causal, p, seed)
+        _, L = attention_fp64(q, k, v, scale, causal)
+        for b in range(2):
+            for h in range(2):
+                keep = philox.dropout_keep(b * 2 + h, np.arange(6), np.arange(10), p, seed)
+                for i in range(6):
+                    acc = np.zeros(4)
+                    for j in range(10):
+                        if causal and j > i + 4:
+                            continue
+                        if keep[i, j]:
+                            acc += math.exp(scale * float(q[b, h, i] @ k[b, h, j]) - L[b, h, i]) * v[b, h, j]
+                    np.testing.assert_allclose(O[b, h, i], acc * 256 / T, rtol=0, atol=1e-12)
+
+
+def pin_unbiased(attn):
+    """The mean over seeds of the dropped-out output approaches the output without dropout:
+    per element |mean − O| <= 6·sqrt(Var/N), Var = (1/kp − 1) Σ_j P_ij² v_j² (independent keeps)."""
+    q, k, v = _qkv(4, B=1, H=1, Lq=4, Lk=16, D=3)
+    p, N, scale = 0.3, 600, 0.7
+    kp = philox.keep_threshold(p) / 256
+    O0, _ = attention_fp64(q, k, v, scale, False)
+    acc = np.zeros_like(O0)
+    for s in range(N):
+        acc += attn(q, k, v, scale, False, p, 1000 + s)[0]
+    mean = acc / N
+    S = scale * q[0, 0] @ k[0, 0].T
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    var = (1 / kp - 1) * (P ** 2) @ (v[0, 0] ** 2)
+    assert np.all(np.abs(mean[0, 0] - O0[0, 0]) <= 6 * np.sqrt(var / N) + 1e-12)
+
+
+PINS = [pin_zero_probability, pin_lse_unaffected, pin_definition_through_lse, pin_unbiased]
+
+
+def _oracle(q, k, v, scale, causal, p, seed):
+    return attention_fp64(q, k, v, scale, causal, chunk=4, dropout_p=p, seed=seed)
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin_holds_for_oracle(pin):
+    pin(_oracle)
+
+
+MUTANTS = {
+    "dropout_unscaled": (" * (256.0 / keep_threshold(dropout_p))", ""),
+    "dropout_before_sum": ("        l = P.sum(axis=1)\n        if dropout_p:", "        if dropout_p:"),
+    "keep_inverted": ("P = P * dropout_keep(", "P = P * ~dropout_keep("),
+    "wrong_head_index": ("dropout_p, seed, b * H + h)", "dropout_p, seed, h)"),
+}
+
+
+def _load_mutant(name):
+    old, new = MUTANTS[name]
+    with open(ATTN_SRC, encoding="utf-8") as f:
+        src = f.read()
+    assert old in src, f"mutation anchor for {name} not found"
+    src = src.replace(old, new, 1)
+    if name == "dropout_before_sum":  # the sum moves after the dropout
+        src = src.replace("* (256.0 / keep_threshold(dropout_p))\n", "* (256.0 / keep_threshold(dropout_p))\n"
+                          "        l = P.sum(axis=1)\n", 1)
+    mod = types.ModuleType(f"oracle.attn_mutant_{name}")
+    mod.__dict__["__name__"] = mod.__name__
+    mod.__dict__["__package__"] = "oracle"
+    sys.modules[mod.__name__] = mod
+    exec(compile(src, ATTN_SRC + f"<{name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    mod = _load_mutant(name)
+
+    def attn(q, k, v, scale, causal, p, seed):
+        return mod.attention_fp64(q, k, v, scale, causal, chunk=4, dropout_p=p, seed=seed)
+
+    failures = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(attn)
+        except Exception as e:
+            failures.append((pin.__name__, type(e).__name__))
+    assert failures, f"no pin catches the planted mistake {name!r}"
