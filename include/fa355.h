@@ -63,7 +63,8 @@ typedef enum {
   FA_ERR_LAUNCH = -9,       /* the kernel launch failed (HIP code in fa_last_hip_error())        */
   FA_ERR_STRIDE = -10,      /* fa_fwd_strided: a stride < 0, or a row stride < D                 */
   FA_ERR_SPLITS = -11,      /* fa_fwd_splitkv: num_splits outside 1..64                          */
-  FA_ERR_WORKSPACE = -12    /* fa_fwd_splitkv / fa_bwd: workspace smaller than its size query    */
+  FA_ERR_WORKSPACE = -12,   /* fa_fwd_splitkv / fa_bwd: workspace smaller than its size query    */
+  FA_ERR_DROPOUT = -13      /* dropout probability outside [0, 1), or round((1-p)*256) == 0      */
 } fa_status;
 
 /*
@@ -199,6 +200,33 @@ size_t fa_bwd_workspace_size(int B, int H, int Lq);
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
            void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
+ * fa_fwd_dropout / fa_bwd_dropout — fa_fwd and fa_bwd with dropout on the
+ * attention weights ([DF §4.1] passes a dropout probability with the call; the
+ * pages give no random number generator, so the generator below is a reading).
+ *
+ *     o[b,h,i,:] = sum_j P_ij * M_ij * v[b,h,j,:],   P_ij = exp(s_ij - lse_i)
+ *
+ * with M_ij = 256/T if the weight is kept and 0 otherwise, T = round((1 -
+ * dropout_p) * 256) in [1, 256] (the keep probability is T/256, so the expected
+ * output is the output without dropout).  lse is that of the scores, as
+ * without dropout.  Keep bits: Philox4x32-10 (Salmon et al., "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011) with key (seed & 0xffffffff, seed >> 32)
+ * and counter (j / 4, i / 4, b*H + h, 0); output word w, byte n is the byte of
+ * row 4*(i/4) + w and key 4*(j/4) + n; the weight is kept iff that byte < T.  The
+ * same seed and dropout_p must be passed to fa_bwd_dropout, whose gradients are
+ * those of this output (the mask is recomputed, never stored).
+ * dropout_p = 0 is exactly fa_fwd / fa_bwd.  Other arguments, layouts and errors
+ * as for fa_fwd and fa_bwd; FA_ERR_DROPOUT for dropout_p outside [0, 1) or T == 0.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+                   int D, float scale, int causal, int dtype, float dropout_p, uint64_t seed, fa_stream_t stream);
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal,
+                   int dtype, float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes,
+                   fa_stream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);

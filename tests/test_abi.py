@@ -49,8 +49,8 @@ def call_strided(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, Lq=64, Lk=6
 
 def test_header_declares_the_abi():
     assert declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-                                    "fa_bwd_workspace_size", "fa_bwd", "fa_status_string", "fa_last_hip_error",
-                                    "fa_version"]
+                                    "fa_bwd_workspace_size", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout",
+                                    "fa_status_string", "fa_last_hip_error", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -65,8 +65,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert fa.fa_version() == 10300
-    for code in range(0, -13, -1):
+    assert fa.fa_version() == 10400
+    for code in range(0, -14, -1):
         s = fa.fa_status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in fa.fa_status_string(5)
@@ -311,3 +311,24 @@ def test_bwd_argument_checks():
     assert call_bwd(Lk=16_776_960) == -2                 # slab beyond 32-bit offsets
     # enough of everything: a later check fails, so nothing launches
     assert call_bwd(ws_bytes=need, causal=1, Lq=600, Lk=500) == -7
+
+
+# ------------------------------------------------------------------------------------------
+# dropout entry points: argument checks (nothing is launched on these paths)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p", [-0.1, 1.0, 1.5, float("nan"), float("inf"), 0.999])
+def test_dropout_probability_checked(p):
+    assert fa.lib.fa_fwd_dropout(*P, 1, 2, 64, 64, 128, 0.125, 0, 1, p, 7, None) == -13
+    args = dict(zip(["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"], PB))
+    need = fa.fa_bwd_workspace_size(1, 2, 64)
+    assert fa.lib.fa_bwd_dropout(args["q"], args["k"], args["v"], args["o"], args["dout"], args["lse"], args["dq"],
+                                 args["dk"], args["dv"], 1, 2, 64, 64, 128, 0.125, 0, 1, p, 7, args["ws"], need,
+                                 None) == -13
+
+
+def test_dropout_entry_points_run_the_common_checks():
+    assert fa.lib.fa_fwd_dropout(None, *P[1:], 1, 2, 64, 64, 128, 0.125, 0, 1, 0.1, 7, None) == -1
+    assert fa.lib.fa_fwd_dropout(*P, 1, 2, 64, 64, 96, 0.125, 0, 1, 0.1, 7, None) == -3
+    assert fa.lib.fa_fwd_dropout(*P, 1, 2, 65, 64, 128, 0.125, 1, 1, 0.1, 7, None) == -7
+    assert fa.lib.fa_fwd_dropout(*P, 1, 2, 64, 64, 128, float("nan"), 0, 1, 0.1, 2 ** 64 - 1, None) == -6

@@ -1,0 +1,100 @@
+"""GPU parity of dropout (fa_fwd_dropout, fa_bwd_dropout through the C ABI) against the fp64 oracle.
+
+The keep bits are integer decisions on Philox4x32-10 bytes, taken identically by
+the kernels and by oracle/philox.py: a single differing bit changes an output row
+by O(1), far beyond the bars.  The bars are those of the dropout-free tests: the
+forward's (2e-3 fp16 / 1e-2 bf16 per element, or one output ulp where larger; LSE
+1e-3) and the backward's (per slab, relative to the slab's max and rms).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import tiled_attention_06_amd as fa
+from oracle import attention_bwd_fp64, attention_fp64
+
+from test_parity import compare as compare_fwd, note
+from test_parity_bwd import compare as compare_bwd
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+CASES = [  # B, H, Lq, Lk, D, dtype, causal, p, seed
+    (1, 2, 300, 300, 128, "bf16", True, 0.1, 1234),
+    (2, 3, 257, 400, 64, "fp16", False, 0.5, 2 ** 63 + 12345),
+    (1, 2, 100, 1000, 128, "fp16", True, 0.3, 77),
+    (1, 1, 1, 777, 64, "bf16", False, 0.9, 5),
+    (1, 2, 520, 520, 64, "bf16", True, 0.25, 99),
+]
+IDS = [f"B{b}H{h}_{lq}x{lk}_D{d}_{dt}_{'c' if c else 'nc'}_p{p}" for b, h, lq, lk, d, dt, c, p, _ in CASES]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal,p,seed", CASES, ids=IDS)
+def test_dropout_forward(B, H, Lq, Lk, D, dtype, causal, p, seed):
+    inp = ai.make_custom(B, H, Lq, Lk, D, dtype, causal, seed=110_000 + Lq + Lk)
+    note(f"dropout fwd B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype} causal={causal} p={p} seed={seed}")
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fa.fa_fwd_dropout(q, k, v, o, lse, causal=causal, scale=inp["scale"], dropout_p=p, seed=seed)
+    _, lse0 = fa.fa_fwd(q, k, v, causal=causal, scale=inp["scale"])
+    torch.cuda.synchronize()
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], causal, dropout_p=p, seed=seed)
+    compare_fwd(o, lse, O_ref, L_ref, dtype, "dropout fwd")
+    assert torch.equal(lse.cpu(), lse0.cpu()), "LSE must not depend on dropout"
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal,p,seed", CASES, ids=IDS)
+def test_dropout_backward(B, H, Lq, Lk, D, dtype, causal, p, seed):
+    inp = ai.make_custom(B, H, Lq, Lk, D, dtype, causal, seed=120_000 + Lq + Lk)
+    do = ai.make_dout((B, H, Lq, D), dtype, seed=130_000 + Lq)
+    note(f"dropout bwd B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype} causal={causal} p={p} seed={seed}")
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=inp["scale"], dropout_p=p, seed=seed)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    fa.fa_bwd(q, k, v, o, do.to(DEV), lse, dq, dk, dv, causal=causal, scale=inp["scale"], dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, inp["scale"], causal, dropout_p=p, seed=seed)
+    compare_bwd((dq.cpu(), dk.cpu(), dv.cpu()), ref, dtype, "dropout bwd")
+
+
+def test_zero_probability_is_the_plain_call():
+    inp = ai.make_custom(1, 2, 333, 333, 128, "bf16", True, seed=140_001)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o1, l1 = fa.fa_fwd(q, k, v, causal=True)
+    o2, l2 = fa.fa_fwd_dropout(q, k, v, causal=True, dropout_p=0.0, seed=123)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.cpu(), o2.cpu()) and torch.equal(l1.cpu(), l2.cpu())
+
+
+def test_flash_attention_dropout_autograd():
+    inp = ai.make_custom(2, 2, 200, 200, 64, "fp16", True, seed=150_001)
+    do = ai.make_dout((2, 2, 200, 64), "fp16", seed=150_002)
+    q, k, v = (inp[n].to(DEV).requires_grad_(True) for n in ("q", "k", "v"))
+    o = fa.flash_attention(q, k, v, causal=True, dropout_p=0.2, seed=4242)
+    o.backward(do.to(DEV))
+    torch.cuda.synchronize()
+    O_ref, _ = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], True, dropout_p=0.2, seed=4242)
+    err = np.abs(o.detach().double().cpu().numpy() - O_ref).max()
+    note(f"  autograd dropout fwd max err {err:.3e}")
+    assert err <= 2e-3
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, inp["scale"], True, dropout_p=0.2, seed=4242)
+    compare_bwd((q.grad.cpu(), k.grad.cpu(), v.grad.cpu()), ref, "fp16", "autograd dropout")
+
+
+def test_keep_fraction_on_gpu():
+    # V = one-hot columns per key block makes O count the kept weight mass; with uniform weights (q = 0)
+    # the dropped-out output averages (256/T)·keep over the keys, whose mean is near 1.
+    B, H, L, D = 1, 4, 1024, 64
+    q = torch.zeros(B, H, L, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.randn(B, H, L, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.ones(B, H, L, D, dtype=torch.bfloat16, device=DEV)
+    o, _ = fa.fa_fwd_dropout(q, k, v, dropout_p=0.5, seed=31337)
+    torch.cuda.synchronize()
+    m = o.float().mean().item()
+    note(f"  mean of dropped-out ones: {m:.4f}")
+    assert abs(m - 1.0) < 0.01

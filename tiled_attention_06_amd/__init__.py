@@ -7,7 +7,8 @@ library is missing, importing this package raises ImportError.
 
 Names follow the C ABI: ``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_status_string``, ``fa_last_hip_error``,
-``fa_version``, ``fa_bwd``, ``fa_bwd_workspace_size``; ``fa_fwd_qkvpacked`` is a
+``fa_version``, ``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_fwd_dropout``,
+``fa_bwd_dropout`` (also reached through ``dropout_p`` of ``fa_fwd`` / ``fa_bwd``); ``fa_fwd_qkvpacked`` is a
 view helper over ``fa_fwd_strided`` for a packed [B, L, 3, H, D] qkv buffer,
 ``suggest_num_splits`` a host heuristic, and ``flash_attention`` an autograd
 function whose forward is ``fa_fwd`` and whose backward is ``fa_bwd``.
@@ -22,7 +23,8 @@ import os
 import torch
 
 __all__ = ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_qkvpacked",
-           "suggest_num_splits", "fa_bwd", "fa_bwd_workspace_size", "flash_attention", "fa_status_string",
+           "suggest_num_splits", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout",
+           "flash_attention", "fa_status_string",
            "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH", "FA_DTYPE_F16", "FA_DTYPE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
@@ -50,6 +52,11 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp] * 9 + [i] * 5 + [ctypes.c_float, i, i, vp, ctypes.c_size_t, vp]
     lib.fa_bwd.restype = i
+    lib.fa_fwd_dropout.argtypes = [vp] * 5 + [i] * 5 + [ctypes.c_float, i, i, ctypes.c_float, ctypes.c_uint64, vp]
+    lib.fa_fwd_dropout.restype = i
+    lib.fa_bwd_dropout.argtypes = [vp] * 9 + [i] * 5 + [ctypes.c_float, i, i, ctypes.c_float, ctypes.c_uint64, vp,
+                                                       ctypes.c_size_t, vp]
+    lib.fa_bwd_dropout.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
@@ -138,7 +145,7 @@ def _launch(strided, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream, sp
 
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
            lse: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
-           stream: torch.cuda.Stream | None = None, num_splits: int = 1):
+           stream: torch.cuda.Stream | None = None, num_splits: int = 1, dropout_p: float = 0.0, seed: int = 0):
     """Enqueue the attention forward pass on ``stream`` (default: torch's current stream of q's device).
 
     q: [B, H, Lq, D]; k, v: [B, H, Lk, D]; fp16/bf16 tensors on one GPU, dense or
@@ -150,9 +157,33 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | 
     ``fa_fwd_strided``; ``num_splits`` > 1 goes through ``fa_fwd_splitkv`` with a
     workspace allocated here (see ``suggest_num_splits``).  Returns (o, lse).
     """
+    if dropout_p:
+        if num_splits != 1:
+            raise ValueError("dropout is served by the single-pass call only (num_splits=1)")
+        return fa_fwd_dropout(q, k, v, o, lse, causal=causal, scale=scale, dropout_p=dropout_p, seed=seed,
+                              stream=stream)
     B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
     dense = all(t.is_contiguous() for t in (q, k, v, o))
     return _launch(not dense, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream, num_splits)
+
+
+def fa_fwd_dropout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
+                   dropout_p: float = 0.0, seed: int = 0, stream: torch.cuda.Stream | None = None):
+    """The C ``fa_fwd_dropout``: dense [B, H, L, D] tensors, dropout probability and 64-bit seed."""
+    B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
+    if not all(t.is_contiguous() for t in (q, k, v, o)):
+        raise ValueError("fa_fwd_dropout takes dense [B, H, L, D] tensors")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    code = lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Lq, Lk,
+                              D, float(scale), 1 if causal else 0, _DTYPES[q.dtype], float(dropout_p),
+                              int(seed) & 0xFFFFFFFFFFFFFFFF, stream.cuda_stream)
+    if code != 0:
+        raise FaError(code)
+    return o, lse
 
 
 def fa_fwd_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
@@ -226,12 +257,14 @@ def fa_bwd_workspace_size(B: int, H: int, Lq: int) -> int:
 def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
            lse: torch.Tensor, dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
            dv: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
-           workspace: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+           workspace: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None, dropout_p: float = 0.0,
+           seed: int = 0):
     """Enqueue the attention backward pass (the C ``fa_bwd``): gradients of o = fa_fwd(q, k, v) for dout.
 
     q, o, dout: [B, H, Lq, D]; k, v: [B, H, Lk, D]; lse: [B, H, Lq] float32 (fa_fwd's outputs o and lse
     for the same q, k, v, scale and causal flag).  All dense (contiguous).  dq, dk, dv are allocated when
-    not given; ``workspace`` (at least ``fa_bwd_workspace_size`` bytes) likewise.  Returns (dq, dk, dv).
+    not given; ``workspace`` (at least ``fa_bwd_workspace_size`` bytes) likewise.  With ``dropout_p`` > 0
+    the call is ``fa_bwd_dropout`` (same probability and seed as the forward pass).  Returns (dq, dk, dv).
     """
     B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
     if tuple(dout.shape) != tuple(q.shape) or dout.dtype != q.dtype or dout.device != q.device:
@@ -252,10 +285,17 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, d
     need = fa_bwd_workspace_size(B, H, Lq)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    code = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D, float(scale),
-                      1 if causal else 0, _DTYPES[q.dtype], workspace.data_ptr(),
-                      workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if dropout_p:
+        code = lib.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D,
+                                  float(scale), 1 if causal else 0, _DTYPES[q.dtype], float(dropout_p),
+                                  int(seed) & 0xFFFFFFFFFFFFFFFF, workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    else:
+        code = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D, float(scale),
+                          1 if causal else 0, _DTYPES[q.dtype], workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), stream.cuda_stream)
     if code != 0:
         raise FaError(code)
     return dq, dk, dv
@@ -263,24 +303,29 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, d
 
 class _FlashAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, causal, scale):
+    def forward(ctx, q, k, v, causal, scale, dropout_p, seed):
         q, k, v = (t.contiguous() for t in (q, k, v))
-        o, lse = fa_fwd(q, k, v, causal=causal, scale=scale)
+        o, lse = fa_fwd(q, k, v, causal=causal, scale=scale, dropout_p=dropout_p, seed=seed)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.causal, ctx.scale = causal, scale
+        ctx.causal, ctx.scale, ctx.dropout_p, ctx.seed = causal, scale, dropout_p, seed
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = fa_bwd(q, k, v, o, do.contiguous(), lse, causal=ctx.causal, scale=ctx.scale)
-        return dq, dk, dv, None, None
+        dq, dk, dv = fa_bwd(q, k, v, o, do.contiguous(), lse, causal=ctx.causal, scale=ctx.scale,
+                            dropout_p=ctx.dropout_p, seed=ctx.seed)
+        return dq, dk, dv, None, None, None, None
 
 
 def flash_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-                    scale: float | None = None) -> torch.Tensor:
-    """o = softmax(scale·q·kᵀ [causal]) · v on [B, H, L, D] tensors, differentiable in q, k and v.
+                    scale: float | None = None, dropout_p: float = 0.0, seed: int | None = None) -> torch.Tensor:
+    """o = dropout(softmax(scale·q·kᵀ [causal])) · v on [B, H, L, D] tensors, differentiable in q, k and v.
 
-    The forward pass is ``fa_fwd`` (o and the per-row LSE are kept), the backward pass ``fa_bwd``.
+    The forward pass is ``fa_fwd`` (o and the per-row LSE are kept), the backward pass ``fa_bwd``; with
+    ``dropout_p`` > 0 the dropout bits come from ``seed`` (drawn from torch's CPU generator when None) and
+    are recomputed, not stored, for the backward pass.
     """
-    return _FlashAttention.apply(q, k, v, causal, scale)
+    if dropout_p and seed is None:
+        seed = int(torch.randint(0, 2 ** 62, (1,)).item())
+    return _FlashAttention.apply(q, k, v, causal, scale, dropout_p, 0 if seed is None else seed)

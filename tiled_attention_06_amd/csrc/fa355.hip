@@ -21,7 +21,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
 constexpr int kMaxSplits = 64;
 
 int launch_status() {
@@ -34,10 +34,10 @@ int launch_status() {
   return FA_ERR_LAUNCH;
 }
 
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, bool DROP>
 int launch(const fa355::FwdParams& p, const fa355::MergeParams& m, hipStream_t stream) {
   using G = fa355::Geo<D>;
-  hipLaunchKernelGGL((fa355::fa_fwd_kernel<D, DT, CAUSAL>), dim3(p.num_wg), dim3(G::NT), 0, stream, p);
+  hipLaunchKernelGGL((fa355::fa_fwd_kernel<D, DT, CAUSAL, DROP>), dim3(p.num_wg), dim3(G::NT), 0, stream, p);
   int st = launch_status();
   if (st != FA_OK || p.n_split == 1) return st;
   constexpr int rows_per_block = 256 / (D / 4);
@@ -47,11 +47,19 @@ int launch(const fa355::FwdParams& p, const fa355::MergeParams& m, hipStream_t s
   return launch_status();
 }
 
-template <int D>
+template <int D, bool DROP>
 int dispatch_dtype(const fa355::FwdParams& p, const fa355::MergeParams& m, int dtype, bool causal, hipStream_t s) {
   if (dtype == FA_DTYPE_BF16)
-    return causal ? launch<D, fa355::DT_BF16, true>(p, m, s) : launch<D, fa355::DT_BF16, false>(p, m, s);
-  return causal ? launch<D, fa355::DT_F16, true>(p, m, s) : launch<D, fa355::DT_F16, false>(p, m, s);
+    return causal ? launch<D, fa355::DT_BF16, true, DROP>(p, m, s) : launch<D, fa355::DT_BF16, false, DROP>(p, m, s);
+  return causal ? launch<D, fa355::DT_F16, true, DROP>(p, m, s) : launch<D, fa355::DT_F16, false, DROP>(p, m, s);
+}
+
+// Dropout keep threshold T = round((1 - p)·256): 256 keeps everything (no
+// dropout), 0 (p too close to 1) and p outside [0, 1) are errors (-1 returned).
+int drop_threshold(float p) {
+  if (!(p >= 0.0f && p < 1.0f)) return -1;
+  const int t = (int)floor((1.0 - (double)p) * 256.0 + 0.5);
+  return t < 1 ? -1 : (t > 256 ? 256 : t);
 }
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
@@ -64,7 +72,8 @@ size_t ws_bytes(int B, int H, int Lq, int D, int splits) {
 
 int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk, int D,
         const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride, const int64_t* o_stride,
-        float scale, int causal, int dtype, int splits, void* ws, size_t ws_size, fa_stream_t stream) {
+        float scale, int causal, int dtype, int splits, void* ws, size_t ws_size, fa_stream_t stream,
+        float dropout_p = 0.0f, uint64_t seed = 0) {
   if (!q || !k || !v || !o || !lse || !q_stride || !k_stride || !v_stride || !o_stride) return FA_ERR_NULL;
   if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
@@ -78,6 +87,8 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     if (st[i][0] % 8 || st[i][1] % 8 || st[i][2] % 8) return FA_ERR_ALIGN;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (causal && Lq > Lk) return FA_ERR_CAUSAL_SHAPE;
+  const int drop_t = drop_threshold(dropout_p);
+  if (drop_t < 0) return FA_ERR_DROPOUT;
   if (splits < 1 || splits > kMaxSplits) return FA_ERR_SPLITS;
   if (splits > 1) {
     if (!ws) return FA_ERR_NULL;
@@ -123,6 +134,10 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   p.c = (float)((scale != 0.0f ? fabs((double)scale) : 1.0) * log2e);
   p.q_and = scale == 0.0f ? 0u : 0xffffffffu;
   p.q_xor = scale < 0.0f ? 0x80008000u : 0u;
+  p.drop_t = (uint32_t)drop_t;
+  p.seed_lo = (uint32_t)seed;
+  p.seed_hi = (uint32_t)(seed >> 32);
+  p.drop_scale = (float)(256.0 / drop_t);
 
   fa355::MergeParams m;
   m.ws_o = p.ws_o;
@@ -136,7 +151,11 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   m.o_sb = p.o_sb, m.o_sh = p.o_sh, m.o_sl = p.o_sl;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return D == 128 ? dispatch_dtype<128>(p, m, dtype, causal != 0, s) : dispatch_dtype<64>(p, m, dtype, causal != 0, s);
+  if (drop_t < 256)  // (only the single-pass entry point takes a dropout probability)
+    return D == 128 ? dispatch_dtype<128, true>(p, m, dtype, causal != 0, s)
+                    : dispatch_dtype<64, true>(p, m, dtype, causal != 0, s);
+  return D == 128 ? dispatch_dtype<128, false>(p, m, dtype, causal != 0, s)
+                  : dispatch_dtype<64, false>(p, m, dtype, causal != 0, s);
 }
 
 // ---- backward
@@ -152,7 +171,7 @@ size_t bwd_ws_bytes(int B, int H, int Lq) {
   return align256((size_t)B * H * lq4(Lq) * 4) + (size_t)B * H * lq4(Lq) * 4;
 }
 
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, bool DROP>
 int launch_bwd(fa355::BwdParams p, hipStream_t stream) {
   constexpr int rows_per_block = 256 / (D / 8);
   const int64_t rows = (int64_t)p.bh * p.Lq4;
@@ -162,25 +181,25 @@ int launch_bwd(fa355::BwdParams p, hipStream_t stream) {
   if (st != FA_OK) return st;
   p.num_wg = p.bh * p.n_qt;
   p.xcd_remap = (p.num_wg % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((fa355::fa_bwd_dq_kernel<D, DT, CAUSAL>), dim3(p.num_wg), dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((fa355::fa_bwd_dq_kernel<D, DT, CAUSAL, DROP>), dim3(p.num_wg), dim3(512), 0, stream, p);
   st = launch_status();
   if (st != FA_OK) return st;
   p.num_wg = p.bh * p.n_kt;
   p.xcd_remap = (p.num_wg % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((fa355::fa_bwd_dkdv_kernel<D, DT, CAUSAL>), dim3(p.num_wg), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa355::fa_bwd_dkdv_kernel<D, DT, CAUSAL, DROP>), dim3(p.num_wg), dim3(256), 0, stream, p);
   return launch_status();
 }
 
-template <int D>
+template <int D, bool DROP>
 int dispatch_bwd(const fa355::BwdParams& p, int dtype, bool causal, hipStream_t s) {
   if (dtype == FA_DTYPE_BF16)
-    return causal ? launch_bwd<D, fa355::DT_BF16, true>(p, s) : launch_bwd<D, fa355::DT_BF16, false>(p, s);
-  return causal ? launch_bwd<D, fa355::DT_F16, true>(p, s) : launch_bwd<D, fa355::DT_F16, false>(p, s);
+    return causal ? launch_bwd<D, fa355::DT_BF16, true, DROP>(p, s) : launch_bwd<D, fa355::DT_BF16, false, DROP>(p, s);
+  return causal ? launch_bwd<D, fa355::DT_F16, true, DROP>(p, s) : launch_bwd<D, fa355::DT_F16, false, DROP>(p, s);
 }
 
 int bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
         void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal, int dtype, void* ws,
-        size_t ws_size, fa_stream_t stream) {
+        size_t ws_size, fa_stream_t stream, float dropout_p = 0.0f, uint64_t seed = 0) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !ws) return FA_ERR_NULL;
   if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
@@ -191,6 +210,8 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
   if (!aligned(lse, 4) || !aligned(ws, 256)) return FA_ERR_ALIGN;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (causal && Lq > Lk) return FA_ERR_CAUSAL_SHAPE;
+  const int drop_t = drop_threshold(dropout_p);
+  if (drop_t < 0) return FA_ERR_DROPOUT;
   if (ws_size < bwd_ws_bytes(B, H, Lq)) return FA_ERR_WORKSPACE;
   // one head's slab plus a tile of padding in 32-bit byte offsets
   if (((int64_t)Lq + 256) * D * 2 >= (1ll << 32) || ((int64_t)Lk + 256) * D * 2 >= (1ll << 32)) return FA_ERR_SHAPE;
@@ -222,8 +243,14 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
   p.xcd_remap = 0;
   p.c = (float)((double)scale * 1.4426950408889634074);
   p.scale = scale;
+  p.drop_t = (uint32_t)drop_t;
+  p.seed_lo = (uint32_t)seed;
+  p.seed_hi = (uint32_t)(seed >> 32);
+  p.drop_scale = (float)(256.0 / drop_t);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return D == 128 ? dispatch_bwd<128>(p, dtype, causal != 0, s) : dispatch_bwd<64>(p, dtype, causal != 0, s);
+  if (drop_t < 256)
+    return D == 128 ? dispatch_bwd<128, true>(p, dtype, causal != 0, s) : dispatch_bwd<64, true>(p, dtype, causal != 0, s);
+  return D == 128 ? dispatch_bwd<128, false>(p, dtype, causal != 0, s) : dispatch_bwd<64, false>(p, dtype, causal != 0, s);
 }
 
 }  // namespace
@@ -270,6 +297,22 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
              stream);
 }
 
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+                   int D, float scale, int causal, int dtype, float dropout_p, uint64_t seed, fa_stream_t stream) {
+  const int64_t sq[3] = {(int64_t)H * Lq * D, (int64_t)Lq * D, D};
+  const int64_t sk[3] = {(int64_t)H * Lk * D, (int64_t)Lk * D, D};
+  return fwd(q, k, v, o, lse, B, H, Lq, Lk, D, sq, sk, sk, sq, scale, causal, dtype, 1, nullptr, 0, stream, dropout_p,
+             seed);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal,
+                   int dtype, float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes,
+                   fa_stream_t stream) {
+  return bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Lq, Lk, D, scale, causal, dtype, workspace, workspace_bytes,
+             stream, dropout_p, seed);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -284,6 +327,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_LAUNCH: return "fa_fwd: kernel launch failed (see fa_last_hip_error)";
     case FA_ERR_STRIDE: return "fa_fwd: strides must be >= 0, with a row stride of at least D";
     case FA_ERR_SPLITS: return "fa_fwd_splitkv: num_splits must be between 1 and 64";
+    case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1) with round((1 - p) * 256) >= 1";
     case FA_ERR_WORKSPACE: return "workspace smaller than the size query returns (fa_fwd_splitkv / fa_bwd)";
     default: return "fa_fwd: unknown status code";
   }

@@ -61,6 +61,10 @@ struct BwdParams {
   int xcd_remap;      // 1: group consecutive work items on one XCD
   float c;            // scale·log2(e) (any sign)
   float scale;
+  // dropout (kernels instantiated with DROP): the forward pass's keep bits
+  // (byte < drop_t), kept weights scaled by drop_scale = 256 / drop_t
+  uint32_t drop_t, seed_lo, seed_hi;
+  float drop_scale;
 };
 
 // The two 16-bit values of a dword as fp32 (exact), low half first.
@@ -146,7 +150,7 @@ __device__ __forceinline__ void bwd_wait_join() {
 // ---------------------------------------------------------------------------
 // dQ: 8 waves x 32 query rows; loop over 64-key tiles
 // ---------------------------------------------------------------------------
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(BwdParams p) {
   using G = Geo<D>;
   constexpr int NW = 8, BR = 256, BC = 64, KB = 2, NB = D / 32, KS = D / 16;
@@ -238,7 +242,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+          // dropout bits of registers 8h..8h+7 (keys 32kb + 16h + 8a + 4g + 0..3 of row qrow)
+          uint32_t dwd[2] = {0u, 0u};
+          if constexpr (DROP) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              const u32x4 w4 = drop_block((j0 + 32 * kb + 16 * h + 8 * a + 4 * g) >> 2, qrow >> 2, bh, p.seed_lo,
+                                          p.seed_hi);
+              const int wi = qrow & 3;
+              dwd[a] = wi == 0 ? w4[0] : wi == 1 ? w4[1] : wi == 2 ? w4[2] : w4[3];
+            }
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float ds[2];
@@ -250,10 +265,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int ko = 32 * kb + 8 * (r >> 2) + (r & 3);
                 pr = ko >= lim ? 0.f : pr;
               }
-              ds[u] = pr * (dP[kb][r] - delta);
+              float dp = dP[kb][r];
+              if constexpr (DROP) {
+                // dP of the weight before dropout: the dropped-out weight's gradient times its factor
+                const uint32_t byte = (dwd[e >> 1] >> (8 * (2 * (e & 1) + u))) & 0xffu;
+                dp = byte < p.drop_t ? dp * p.drop_scale : 0.f;
+              }
+              ds[u] = pr * (dp - delta);
             }
             db[kb][h][e] = pack2<DT>(ds[0], ds[1]);
           }
+        }
       // dQᵀ += Kᵀ·dSᵀ: A = 8 keys of one head dim (two transposing reads)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -287,7 +309,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // ---------------------------------------------------------------------------
 // dK, dV: 4 waves x 32 keys; loop over 64-row query tiles
 // ---------------------------------------------------------------------------
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_dkdv_kernel(BwdParams p) {
   using G = Geo<D>;
   constexpr int NW = 4, BKV = 128, BQ = 64, QB = 2, NB = D / 32, KS = D / 16;
@@ -389,7 +411,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     u32x4 pb[2], db[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      // dropout bits of registers 8h..8h+7: rows i0 + 32qb + 8a + 4g + 0..3 (a = 2h, 2h+1)
+      // of this lane's key; word w of a block holds row 4*(row/4) + w, byte key % 4
+      u32x4 dw[2];
+      if constexpr (DROP) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          dw[a] = drop_block(key >> 2, (i0 + 32 * qb + 16 * h + 8 * a + 4 * g) >> 2, bh, p.seed_lo, p.seed_hi);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float pp[2], ds[2];
@@ -402,12 +432,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int row = i0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
             pr = key > row + off ? 0.f : pr;
           }
-          pp[u] = pr;
-          ds[u] = pr * (dP[r] - de[r >> 2][r & 3]);
+          float dp = dP[r];
+          if constexpr (DROP) {
+            const uint32_t byte = (dw[e >> 1][2 * (e & 1) + u] >> (8 * (key & 3))) & 0xffu;
+            const float f = byte < p.drop_t ? p.drop_scale : 0.f;
+            pp[u] = pr * f;   // the dropped-out weight multiplies dO in dV
+            dp *= f;          // dP of the weight before dropout
+          } else {
+            pp[u] = pr;
+          }
+          ds[u] = pr * (dp - de[r >> 2][r & 3]);
         }
         pb[h][e] = pack2<DT>(pp[0], pp[1]);
         db[h][e] = pack2<DT>(ds[0], ds[1]);
       }
+    }
     // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS: A = 8 rows of one head dim (transposing reads)
 #pragma unroll
     for (int h = 0; h < 2; ++h)

@@ -105,7 +105,43 @@ struct FwdParams {
   float c;          // |scale| * log2(e), or log2(e) when scale == 0 (always > 0)
   uint32_t q_and;   // 0xffffffff, or 0 when scale == 0 (Q forced to zero)
   uint32_t q_xor;   // 0x80008000 when scale < 0 (Q negated exactly), else 0
+  // dropout (kernels instantiated with DROP): keep iff mask byte < drop_t; kept
+  // weights scaled by drop_scale = 256 / drop_t; Philox key (seed_lo, seed_hi)
+  uint32_t drop_t, seed_lo, seed_hi;
+  float drop_scale;
 };
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit products, the high
+// halves xored into the other two words with the key, and the key advanced by
+// the Weyl constants between rounds.
+__device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                          uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = c0 * 0xD2511F53u, hi0 = __umulhi(c0, 0xD2511F53u);
+    const uint32_t lo1 = c2 * 0xCD9E8D57u, hi1 = __umulhi(c2, 0xCD9E8D57u);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// Dropout bits of a 4 x 4 block of (query row, key) of one (batch, head): the
+// counter is (key / 4, row / 4, batch*head, 0); output word w, byte b covers row
+// 4*(row/4) + w and key 4*(key/4) + b.  A weight is kept iff its byte < T.
+__device__ __forceinline__ u32x4 drop_block(int key4, int row4, int bh, uint32_t k0, uint32_t k1) {
+  return philox10((uint32_t)key4, (uint32_t)row4, (uint32_t)bh, 0u, k0, k1);
+}
+// 16-bit lane masks of the kept weights of word w's bytes b0 and b0+1
+__device__ __forceinline__ uint32_t keep_pair(uint32_t w, int b0, uint32_t T) {
+  const uint32_t lo = (w >> (8 * b0)) & 0xffu, hi = (w >> (8 * b0 + 8)) & 0xffu;
+  return (lo < T ? 0x0000ffffu : 0u) | (hi < T ? 0xffff0000u : 0u);
+}
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -246,7 +282,7 @@ struct Geo {
   static_assert(LDS <= 163840, "one workgroup per CU");
 };
 
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(FwdParams p) {
   using G = Geo<D>;
   constexpr int BC = G::BC, KB = G::KB, NB = G::NB, KS = G::KS, NCH = G::NCH;
@@ -478,13 +514,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto rescale = [&](float m_tile) { scale_o(move_max(m_tile)); };
   // weights of a tile against the running max, and their two row sums.  Every
   // row sees key 0 in tile 0, so m_run is finite from the first tile on.
-  auto make_p = [&](const f32x16(&S)[KB], u32x4(&pb)[KB][2]) {
+  // With DROP, the weights that multiply V are masked by the dropout bits of
+  // their (row, key); the sums stay those of all weights (dropout acts on the
+  // normalised weights, and LSE is that of the scores).
+  auto make_p = [&](const f32x16(&S)[KB], u32x4(&pb)[KB][2], int t) {
     const float mb = m_run;
     float sf = 0.f, sr = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        // keys of registers 8h..8h+7: 32kb + 16h + 4g + {0..3} and + 8 + 4g + {0..3}
+        u32x4 dw[2];
+        if constexpr (DROP) {
+          const int lane_d = opaque(tid) & 63;
+          const int row_d = i0w + (lane_d & 31), g_d = lane_d >> 5;
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const u32x4 w4 = drop_block((t * BC + 32 * kb + 16 * h + 8 * a + 4 * g_d) >> 2, row_d >> 2, bh,
+                                        p.seed_lo, p.seed_hi);
+            const int wi = row_d & 3;
+            const uint32_t w = wi == 0 ? w4[0] : wi == 1 ? w4[1] : wi == 2 ? w4[2] : w4[3];
+            dw[a] = u32x4{keep_pair(w, 0, p.drop_t), keep_pair(w, 2, p.drop_t), 0u, 0u};
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * h + 2 * e], c, -mb));
@@ -492,8 +545,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           sf += p0 + p1;
           const uint32_t pk = pack2<DT>(p0, p1);
           sr = sum2<DT>(pk, sr);
-          pb[kb][h][e] = pk;
+          if constexpr (DROP)
+            pb[kb][h][e] = pk & dw[e >> 1][e & 1];
+          else
+            pb[kb][h][e] = pk;
         }
+      }
     l_f += sf;
     l_r += sr;
   };
@@ -560,7 +617,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       compute_s(kst(PN{}), Sn);
       u32x4 pb[KB][2];
-      make_p(Sc, pb);
+      make_p(Sc, pb, t);
       pv(pb, vst(Pc));
       mxn = row_max(Sn);
       end_iter(t);
@@ -578,7 +635,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       rescale(mxc);
       if (tf + G::NS - 1 < t_e) copies_rt(tf);
       u32x4 pb[KB][2];
-      make_p(Sc, pb);
+      make_p(Sc, pb, tf);
       pv(pb, vst_rt((tf - t_b) % G::NS));
       end_iter(tf);
     };
@@ -600,7 +657,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       mask_tile(sA, t);
       const bool any = move_max(row_max(sA));
       u32x4 pb[KB][2];
-      make_p(sA, pb);
+      make_p(sA, pb, t);
       scale_o(any);
       __builtin_amdgcn_sched_barrier(0);
       pv(pb, vst_rt((t - t_b) % G::NS));
@@ -635,7 +692,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return;
   }
   // one pass: normalise by the sum of the rounded weights, store O and LSE
-  const float inv = 1.0f / lr_t;
+  const float inv = DROP ? p.drop_scale / lr_t : 1.0f / lr_t;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
