@@ -48,15 +48,18 @@ def run_bwd(inp, do, causal, scale=None):
     return dq.cpu(), dk.cpu(), dv.cpu()
 
 
-def compare(got, ref, dtype, what, heads=None):
+def compare(got, ref, dtype, what, heads=None, extra=None):
+    """extra: optional {(b, h): (dq row bounds, dk row bounds)} added to the bars (see bwd_bounds)."""
     names = ("dq", "dk", "dv")
-    for name, g, r in zip(names, got, ref):
+    for t, (name, g, r) in enumerate(zip(names, got, ref)):
         g = g.double().numpy()
         pairs = heads if heads is not None else [(b, h) for b in range(g.shape[0]) for h in range(g.shape[1])]
         for b, h in pairs:
             gs, rs = g[b, h], r[b, h]
             assert np.isfinite(gs).all(), f"{what} {name} ({b},{h}): non-finite (unwritten?)"
             err = np.abs(gs - rs)
+            if extra is not None and t < 2:
+                err = np.maximum(err - extra[(b, h)][t], 0.0)  # what the rounding of O does not explain
             mx, rms = np.abs(rs).max(), np.sqrt((rs ** 2).mean())
             e_max, e_rms = err.max(), np.sqrt((err ** 2).mean())
             note(f"  {what} {name} ({b},{h}): max err {e_max:.3e} (max |ref| {mx:.3e}), rms err {e_rms:.3e} "
@@ -120,6 +123,25 @@ def test_bwd_sum_rules_at_train_shape():
     note("bwd train7b_4k: oracle on two heads")
     ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, w.scale, True, heads=heads)
     compare(got, ref, w.dtype, "bwd train7b_4k", heads=heads)
+
+
+def test_bwd_peaked_softmax():
+    # the numerics-stress recipe (Q ~ N(0, 3²) boosted so one key per row leads by 20 logits) at L = 1024:
+    # dQ and dK are then ~1e-7, of the order of what rounding the stored O moves Δ by (bwd_bounds)
+    import dataclasses
+
+    from bwd_bounds import delta_bounds
+    from oracle import attention_fp64
+
+    w = dataclasses.replace(ai.WORKLOADS["stress_8k"], B=1, H=2, Lq=1024, Lk=1024)
+    inp = ai.make_inputs(w)
+    do = ai.make_dout((1, 2, 1024, 64), "bf16", seed=95_001)
+    note("bwd peaked softmax (stress recipe, L=1024)")
+    got = run_bwd(inp, do, False)
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, w.scale, False)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, False)
+    extra = delta_bounds(inp["q"], inp["k"], do, O_ref, L_ref, w.scale, False, "bf16", [(0, 0), (0, 1)])
+    compare(got, ref, "bf16", "bwd peaked", extra=extra)
 
 
 def test_bwd_deterministic():
