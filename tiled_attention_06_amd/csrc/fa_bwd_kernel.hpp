@@ -400,91 +400,113 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       dP = mfma32<DT>(lds_read16(orb + k_off + row_off(32 * qb, KBS) + 32 * s), vr[s], dP);
     }
   };
-  auto grads = [&](auto MASK, int qb, int i0, const f32x16& S, const f32x16& dP, const unsigned char* qtb,
-                   const unsigned char* otb, const float* lsb, const float* deb) {
-    // LSE·log2(e) and Δ of the lane's rows: tile rows 32qb + 8a + 4g + 0..3
-    f32x4 ls[4], de[4];
+  // The weights and dS of one register pair (h, e) of half qb: registers
+  // r = 8h + 2e + u, rows 32qb + 8(r/4) + 4g + r%4 of the tile, this lane's key.
+  // dw: the dropout words of rows group a = 2h + e/2 (DROP only).
+  auto valu_pair = [&](auto MASK, int qb, int h, int e, int i0, const f32x16& S, const f32x16& dP,
+                       const f32x4 (&ls)[4], const f32x4 (&de)[4], const u32x4& dw, u32x4 (&pb)[2],
+                       u32x4 (&db)[2]) {
+    float pp[2], ds[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 8 * h + 2 * e + u;
+      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -ls[r >> 2][r & 3]));
+      if constexpr (decltype(MASK)::value) {
+        // key j0w + l32 visible to row i iff j <= i + off
+        const int row = i0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+        pr = key > row + off ? 0.f : pr;
+      }
+      float dp = dP[r];
+      if constexpr (DROP) {
+        const uint32_t byte = (dw[2 * (e & 1) + u] >> (8 * (key & 3))) & 0xffu;
+        const float f = byte < p.drop_t ? p.drop_scale : 0.f;
+        pp[u] = pr * f;   // the dropped-out weight multiplies dO in dV
+        dp *= f;          // dP of the weight before dropout
+      } else {
+        pp[u] = pr;
+      }
+      ds[u] = pr * (dp - de[r >> 2][r & 3]);
+    }
+    pb[h][e] = pack2<DT>(pp[0], pp[1]);
+    db[h][e] = pack2<DT>(ds[0], ds[1]);
+  };
+  auto load_stats = [&](int qb, const float* lsb, const float* deb, f32x4 (&ls)[4], f32x4 (&de)[4]) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       ls[a] = *(const f32x4*)(lsb + 32 * qb + 8 * a + 4 * g);
       de[a] = *(const f32x4*)(deb + 32 * qb + 8 * a + 4 * g);
     }
-    u32x4 pb[2], db[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // dropout bits of registers 8h..8h+7: rows i0 + 32qb + 8a + 4g + 0..3 (a = 2h, 2h+1)
-      // of this lane's key; word w of a block holds row 4*(row/4) + w, byte key % 4
-      u32x4 dw[2];
-      if constexpr (DROP) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-          dw[a] = drop_block(key >> 2, (i0 + 32 * qb + 16 * h + 8 * a + 4 * g) >> 2, bh, p.seed_lo, p.seed_hi);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float pp[2], ds[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 8 * h + 2 * e + u;
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], c, -ls[r >> 2][r & 3]));
-          if constexpr (decltype(MASK)::value) {
-            // key j0w + l32 visible to row i iff j <= i + off
-            const int row = i0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-            pr = key > row + off ? 0.f : pr;
-          }
-          float dp = dP[r];
-          if constexpr (DROP) {
-            const uint32_t byte = (dw[e >> 1][2 * (e & 1) + u] >> (8 * (key & 3))) & 0xffu;
-            const float f = byte < p.drop_t ? p.drop_scale : 0.f;
-            pp[u] = pr * f;   // the dropped-out weight multiplies dO in dV
-            dp *= f;          // dP of the weight before dropout
-          } else {
-            pp[u] = pr;
-          }
-          ds[u] = pr * (dp - de[r >> 2][r & 3]);
-        }
-        pb[h][e] = pack2<DT>(pp[0], pp[1]);
-        db[h][e] = pack2<DT>(ds[0], ds[1]);
-      }
-    }
-    // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS: A = 8 rows of one head dim (transposing reads)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const unsigned char* ao = otb + t_off + 64 * nb;
-        const u32x2 olo = lds_read_tr(ao + row_off(32 * qb + 16 * h, VBS));
-        const u32x2 ohi = lds_read_tr(ao + row_off(32 * qb + 16 * h + 8, VBS));
-        dv[nb] = mfma32<DT>(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pb[h], dv[nb]);
-        const unsigned char* aq = qtb + t_off + 64 * nb;
-        const u32x2 qlo = lds_read_tr(aq + row_off(32 * qb + 16 * h, VBS));
-        const u32x2 qhi = lds_read_tr(aq + row_off(32 * qb + 16 * h + 8, VBS));
-        dk[nb] = mfma32<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, db[h], dk[nb]);
-      }
   };
-  // D = 64, full tiles: the products of both halves first (four independent MFMA
-  // chains), so that the MFMAs of one half can overlap the VALU work of the other
-  // (measured faster at D = 64, slower at D = 128).  Otherwise one half after the
-  // other (fewer live registers).
+  auto drop_words = [&](int qb, int h, int a, int i0) -> u32x4 {
+    if constexpr (DROP)
+      return drop_block(key >> 2, (i0 + 32 * qb + 16 * h + 8 * a + 4 * g) >> 2, bh, p.seed_lo, p.seed_hi);
+    else
+      return u32x4{};
+  };
+  // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS for register half h, dims block nb of half qb
+  auto grad_mfma = [&](int qb, int h, int nb, const u32x4 (&pb)[2], const u32x4 (&db)[2],
+                       const unsigned char* qtb, const unsigned char* otb) {
+    const unsigned char* ao = otb + t_off + 64 * nb;
+    const u32x2 olo = lds_read_tr(ao + row_off(32 * qb + 16 * h, VBS));
+    const u32x2 ohi = lds_read_tr(ao + row_off(32 * qb + 16 * h + 8, VBS));
+    dv[nb] = mfma32<DT>(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pb[h], dv[nb]);
+    const unsigned char* aq = qtb + t_off + 64 * nb;
+    const u32x2 qlo = lds_read_tr(aq + row_off(32 * qb + 16 * h, VBS));
+    const u32x2 qhi = lds_read_tr(aq + row_off(32 * qb + 16 * h + 8, VBS));
+    dk[nb] = mfma32<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, db[h], dk[nb]);
+  };
+  // One 64-row query tile, software-pipelined over its two 32-row halves so that
+  // with one wave per SIMD the MFMAs of one stage overlap the VALU work of
+  // another (the program order fixes the interleave, scheduling barriers keep it):
+  //   S0, dP0  |  S1, dP1 (MFMA) with weights/dS of half 0 (VALU)
+  //            |  dV, dK of half 0 (MFMA) with weights/dS of half 1 (VALU)
+  //            |  dV, dK of half 1 (MFMA)
+  // In S and dP the lane holds key l%32 and rows 32qb + 8(r/4) + 4g + r%4.
+  constexpr int PAIRS = 8;                    // (h, e) register pairs per half
+  constexpr int PPS = PAIRS / KS;             // pairs per S/dP step
+  constexpr int GSTEPS = 2 * NB;              // (h, nb) dV/dK steps per half
+  constexpr int PPG = PAIRS / GSTEPS;         // pairs per dV/dK step
+  static_assert(PAIRS % KS == 0 && PAIRS % GSTEPS == 0, "interleave");
   auto tile_body = [&](auto MASK, int i0, const unsigned char* qrb, const unsigned char* qtb,
                        const unsigned char* orb, const unsigned char* otb, const float* lsb, const float* deb) {
-    if constexpr (decltype(MASK)::value || D == 128) {
+    f32x16 S0, dP0, S1 = f32x16{}, dP1 = f32x16{};
+    products(0, qrb, orb, S0, dP0);
+    u32x4 pb0[2], db0[2], pb1[2], db1[2];
+    {
+      f32x4 ls[4], de[4];
+      load_stats(0, lsb, deb, ls, de);
+      u32x4 dw{};
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        f32x16 S, dP;
-        products(qb, qrb, orb, S, dP);
-        grads(MASK, qb, i0, S, dP, qtb, otb, lsb, deb);
-        // (a scheduling barrier per half: operand reads of the next half are not
-        // hoisted over this one, which would run out of registers)
+      for (int s = 0; s < KS; ++s) {
+        S1 = mfma32<DT>(lds_read16(qrb + k_off + row_off(32, KBS) + 32 * s), kr[s], S1);
+        dP1 = mfma32<DT>(lds_read16(orb + k_off + row_off(32, KBS) + 32 * s), vr[s], dP1);
+#pragma unroll
+        for (int j = 0; j < PPS; ++j) {
+          const int pr = s * PPS + j, h = pr >> 2, e = pr & 3;
+          if ((e & 1) == 0) dw = drop_words(0, h, e >> 1, i0);
+          valu_pair(MASK, 0, h, e, i0, S0, dP0, ls, de, dw, pb0, db0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
-      f32x16 S0, dP0, S1, dP1;
-      products(0, qrb, orb, S0, dP0);
-      products(1, qrb, orb, S1, dP1);
-      grads(MASK, 0, i0, S0, dP0, qtb, otb, lsb, deb);
-      grads(MASK, 1, i0, S1, dP1, qtb, otb, lsb, deb);
     }
+    {
+      f32x4 ls[4], de[4];
+      load_stats(1, lsb, deb, ls, de);
+      u32x4 dw{};
+#pragma unroll
+      for (int st = 0; st < GSTEPS; ++st) {
+        grad_mfma(0, st / NB, st % NB, pb0, db0, qtb, otb);
+#pragma unroll
+        for (int j = 0; j < PPG; ++j) {
+          const int pr = st * PPG + j, h = pr >> 2, e = pr & 3;
+          if ((e & 1) == 0) dw = drop_words(1, h, e >> 1, i0);
+          valu_pair(MASK, 1, h, e, i0, S1, dP1, ls, de, dw, pb1, db1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < GSTEPS; ++st) grad_mfma(1, st / NB, st % NB, pb1, db1, qtb, otb);
   };
 
   bwd_wait_join();
