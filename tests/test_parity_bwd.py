@@ -144,6 +144,25 @@ def test_bwd_peaked_softmax():
     compare(got, ref, "bf16", "bwd peaked", extra=extra)
 
 
+@pytest.mark.parametrize("name", ["llama7b_2k", "stress_8k", "long_16k"])
+def test_bwd_workload_sampled(name):
+    # the other workloads at full size: every head on the GPU, one or two heads in full against the oracle
+    from bwd_bounds import delta_bounds
+    from oracle import attention_fp64
+
+    w = ai.WORKLOADS[name]
+    inp = ai.make_inputs(w)
+    do = ai.make_dout((w.B, w.H, w.Lq, w.D), w.dtype, seed=w.seed + 100)
+    note(f"bwd {name}: GPU")
+    got = run_bwd(inp, do, w.causal)
+    heads = [(w.B - 1, w.H - 1)] if name == "long_16k" else [(0, 0), (w.B - 1, w.H - 1)]
+    note(f"bwd {name}: oracle on {heads}")
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, w.scale, w.causal, heads=heads)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, w.causal, heads=heads)
+    extra = delta_bounds(inp["q"], inp["k"], do, O_ref, L_ref, w.scale, w.causal, w.dtype, heads)
+    compare(got, ref, w.dtype, f"bwd {name}", heads=heads, extra=extra)
+
+
 def test_bwd_deterministic():
     inp = ai.make_custom(1, 4, 700, 700, 128, "bf16", True, seed=90_001)
     do = ai.make_dout((1, 4, 700, 128), "bf16", seed=90_002)

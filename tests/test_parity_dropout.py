@@ -98,3 +98,26 @@ def test_keep_fraction_on_gpu():
     m = o.float().mean().item()
     note(f"  mean of dropped-out ones: {m:.4f}")
     assert abs(m - 1.0) < 0.01
+
+
+def test_dropout_train_shape_sampled():
+    # the 7B 4K training shape with p = 0.1: forward rows and backward heads sampled against the oracle
+    from test_parity import _sample
+
+    w = ai.WORKLOADS["train7b_4k"]
+    inp = ai.make_inputs(w)
+    do = ai.make_dout((w.B, w.H, w.Lq, w.D), w.dtype, seed=w.seed + 100)
+    p, seed = 0.1, 2024
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd_dropout(q, k, v, causal=True, scale=w.scale, dropout_p=p, seed=seed)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do.to(DEV), lse, causal=True, scale=w.scale, dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    heads, rows = _sample(w, seed=11)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, True, rows=rows, heads=heads,
+                                  dropout_p=p, seed=seed)
+    oc, lc = o.cpu(), lse.cpu()
+    for b, h in heads:
+        compare_fwd(oc[b, h][rows], lc[b, h][rows], O_ref[b, h], L_ref[b, h], w.dtype, f"dropout train ({b},{h})")
+    bh = [(0, 0), (w.B - 1, w.H - 1)]
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, w.scale, True, heads=bh, dropout_p=p, seed=seed)
+    compare_bwd((dq.cpu(), dk.cpu(), dv.cpu()), ref, w.dtype, "dropout train bwd", heads=bh)
