@@ -47,8 +47,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (bf16 causal, L=4096, D=128) and % of MFMA peak"
-KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_06_amd", "csrc", f) for f in ("fa_fwd_kernel.hpp", "fa355.hip")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_train7b_4k_traffic.md")
+_CSRC = os.path.join(ROOT, "tiled_attention_06_amd", "csrc")
+KERNEL_SOURCES = {"fwd": [os.path.join(_CSRC, f) for f in ("fa_fwd_kernel.hpp", "fa355.hip")],
+                  "bwd": [os.path.join(_CSRC, f) for f in ("fa_fwd_kernel.hpp", "fa_bwd_kernel.hpp", "fa355.hip")]}
+TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "fa_fwd_kernel_train7b_4k_traffic.md"),
+                 "bwd": os.path.join(ROOT, "profiles", "fa_bwd_kernels_train7b_4k_traffic.md")}
 
 
 def trace_file(workload: str, pass_: str = "fwd") -> str:
@@ -63,23 +66,24 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(pass_: str = "fwd") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[pass_]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
-    if workload != "train7b_4k" or not os.path.exists(TRAFFIC_FILE):
+def committed_traffic(workload: str, pass_: str = "fwd"):
+    """HBM bytes per call from the committed counter summary, if it matches the current kernels."""
+    path = TRAFFIC_FILES[pass_]
+    if workload != "train7b_4k" or not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE, encoding="utf-8") as f:
+    with open(path, encoding="utf-8") as f:
         text = f.read()
     m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not b or m.group(1) != kernel_source_hash():
+    if not m or not b or m.group(1) != kernel_source_hash(pass_):
         return None
     return float(b.group(1))
 
@@ -185,8 +189,9 @@ def sampled_parity(inp, o, lse, n_rows: int = 128, dropout_p: float = 0.0) -> di
             "tol_o": tol, "tol_lse": 1e-3, "pass": bool(eo <= tol and el <= 1e-3)}
 
 
-def traffic_probe(w, steps: int) -> None:
-    """One plain device copy of COPY_BYTES (the counter calibration), then `steps` launches."""
+def traffic_probe(w, steps: int, pass_: str = "fwd") -> None:
+    """One plain device copy of COPY_BYTES (the counter calibration), then `steps` calls of fa_fwd (or, for
+    pass_ == "bwd", one fa_fwd and then `steps` calls of fa_bwd)."""
     import torch
 
     import attn_inputs
@@ -203,10 +208,18 @@ def traffic_probe(w, steps: int) -> None:
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    for _ in range(steps):
+    if pass_ == "bwd":
+        do = attn_inputs.make_dout((w.B, w.H, w.Lq, w.D), w.dtype, seed=w.seed + 100).to(dev)
         fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale)
+        grads = tuple(torch.empty_like(t) for t in (q, k, v))
+        ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.Lq), dtype=torch.uint8, device=dev)
+        for _ in range(steps):
+            fa.fa_bwd(q, k, v, o, do, lse, *grads, causal=w.causal, scale=w.scale, workspace=ws)
+    else:
+        for _ in range(steps):
+            fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize(dev)
-    log(f"traffic probe: 1 copy of {COPY_BYTES} B, {steps} launches of fa_fwd on {w.name}")
+    log(f"traffic probe: 1 copy of {COPY_BYTES} B, {steps} calls of fa_{pass_} on {w.name}")
 
 
 def _csv_rows(directory: str, name: str):
@@ -220,53 +233,67 @@ def _csv_rows(directory: str, name: str):
     return rows
 
 
-def summarize_traffic(directory: str, w) -> str:
-    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of fa_fwd by the copy kernel's reading."""
+def summarize_traffic(directory: str, w, pass_: str = "fwd") -> str:
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the pass's kernels by the copy kernel's reading."""
     rows = _csv_rows(directory, "*counter_collection.csv")
     per = {}
     for r in rows:
         per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
-    fa_ = [c for (kn, _), c in per.items() if "fa_fwd_kernel" in kn]
-    if not fa_:
-        raise SystemExit("no fa_fwd_kernel dispatches in the counter CSVs")
+    ours = ("fa_fwd_kernel",) if pass_ == "fwd" else ("fa_bwd_prep_kernel", "fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel")
+    mine = {name: [c for (kn, _), c in per.items() if name in kn] for name in ours}
+    if not all(mine.values()):
+        raise SystemExit(f"no dispatches of {[n for n, c in mine.items() if not c]} in the counter CSVs")
     # Calibration dispatches: the fill and the elementwise kernel each write
     # COPY_BYTES, and only the elementwise kernel also reads COPY_BYTES.
-    other = [c for (kn, _), c in per.items() if "fa_fwd_kernel" not in kn]
+    other = [c for (kn, _), c in per.items() if "fa355" not in kn]
     half_kib = COPY_BYTES / 2 / 1024
     cf = [c["FETCH_SIZE"] for c in other if c.get("FETCH_SIZE", 0) > half_kib]
     cw = [c["WRITE_SIZE"] for c in other if c.get("WRITE_SIZE", 0) > half_kib]
-    ff = [c["FETCH_SIZE"] for c in fa_ if "FETCH_SIZE" in c]
-    fw = [c["WRITE_SIZE"] for c in fa_ if "WRITE_SIZE" in c]
-    if not (cf and cw and ff and fw):
-        raise SystemExit("need FETCH_SIZE and WRITE_SIZE for both the copy and fa_fwd")
+    if not (cf and cw):
+        raise SystemExit("need FETCH_SIZE and WRITE_SIZE for the copy")
     kf = COPY_BYTES / (sum(cf) / len(cf) * 1024)   # true bytes per counted byte, reads
     kw = COPY_BYTES / (sum(cw) / len(cw) * 1024)   # and writes
-    fetch = sum(ff) / len(ff) * 1024 * kf
-    write = sum(fw) / len(fw) * 1024 * kw
-    alg = w.hbm_bytes
+    detail, fetch, write = [], 0.0, 0.0
+    for name, cs in mine.items():
+        ff = [c["FETCH_SIZE"] for c in cs if "FETCH_SIZE" in c]
+        fw = [c["WRITE_SIZE"] for c in cs if "WRITE_SIZE" in c]
+        if not (ff and fw):
+            raise SystemExit(f"need FETCH_SIZE and WRITE_SIZE for {name}")
+        f_, w_ = sum(ff) / len(ff) * 1024 * kf, sum(fw) / len(fw) * 1024 * kw
+        fetch, write = fetch + f_, write + w_
+        detail.append(f"{name}: FETCH_SIZE {sum(ff) / len(ff):.1f} KiB, WRITE_SIZE {sum(fw) / len(fw):.1f} KiB per "
+                      f"dispatch -> read {f_:.4g} B, write {w_:.4g} B")
+    bhd = w.B * w.H * w.D
+    if pass_ == "fwd":
+        alg = w.hbm_bytes
+        alg_what = "Q, K, V read once, O and LSE written once"
+    else:
+        alg = 2 * (3 * bhd * w.Lq + 2 * bhd * w.Lk) + 2 * (bhd * w.Lq + 2 * bhd * w.Lk) + 4 * w.B * w.H * w.Lq
+        alg_what = "Q, O, dO, K, V and LSE read once, dQ, dK, dV written once"
+    probe = "--traffic-probe" if pass_ == "fwd" else "--pass bwd --traffic-probe"
     lines = [
-        f"# HBM traffic of fa_fwd_kernel on {w.name} ({w.description})",
+        f"# HBM traffic of {' + '.join(ours)} on {w.name} ({w.description})",
         "",
-        "Counters from two `rocprofv3 --pmc` runs of `bench.py --traffic-probe`: a fill of",
+        f"Counters from two `rocprofv3 --pmc` runs of `bench.py {probe}`: a fill of",
         f"{COPY_BYTES} bytes, a plain elementwise copy of {COPY_BYTES} bytes to another buffer, then",
-        f"{len(ff)} launches of fa_fwd.  Values are KiB per dispatch.  Each counter is scaled by",
+        f"calls of fa_{pass_}.  Values are KiB per dispatch.  Each counter is scaled by",
         "the calibration kernels' true bytes / counted bytes.",
         "",
         "Commands (from the repository root on the GPU box):",
         "",
-        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic_fetch -o t -- python3 bench.py --traffic-probe",
-        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic_write -o t -- python3 bench.py --traffic-probe",
-        f"    python3 bench.py --summarize-traffic gpurun_out  (reads both directories)",
+        f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic_fetch -o t -- python3 bench.py {probe}",
+        f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic_write -o t -- python3 bench.py {probe}",
+        f"    python3 bench.py{' --pass bwd' if pass_ == 'bwd' else ''} --summarize-traffic gpurun_out  (reads both directories)",
         "",
         f"calibration: FETCH_SIZE {sum(cf) / len(cf):.1f} KiB (mean of {len(cf)}), WRITE_SIZE "
         f"{sum(cw) / len(cw):.1f} KiB (mean of {len(cw)}) for {COPY_BYTES / 1024:.0f} KiB moved -> "
         f"read factor {kf:.4f}, write factor {kw:.4f}",
-        f"fa_fwd: FETCH_SIZE {sum(ff) / len(ff):.1f} KiB, WRITE_SIZE {sum(fw) / len(fw):.1f} KiB per dispatch",
-        f"scaled: read {fetch:.4g} B, write {write:.4g} B per launch",
-        f"algorithmic bytes per launch (Q, K, V read once, O and LSE written once): {alg}",
+        *detail,
+        f"scaled: read {fetch:.4g} B, write {write:.4g} B per call",
+        f"algorithmic bytes per call ({alg_what}): {alg}",
         f"traffic / algorithmic: {(fetch + write) / alg:.3f}",
         "",
-        f"kernel_source_sha256: {kernel_source_hash()}",
+        f"kernel_source_sha256: {kernel_source_hash(pass_)}",
         f"hbm_bytes_per_launch: {fetch + write:.6g}",
         "",
     ]
@@ -307,7 +334,7 @@ def summarize_trace(directory: str, w, bench_line: str | None, pass_: str = "fwd
     lines += ["| " + " | ".join(str(r[h]) for h in hdr) + " |" for r in keep]
     if bench_line:
         lines += ["", "bench.py JSON line of the same profiled run:", "", "    " + bench_line.strip()]
-    lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    lines += ["", f"kernel_source_sha256: {kernel_source_hash(pass_)}", ""]
     return "\n".join(lines)
 
 
@@ -369,7 +396,8 @@ def bench_bwd(args, w) -> int:
                    "flop_per_step": flops, "dropout_p": args.dropout},
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 5), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
+                     "traffic": committed_traffic(w.name, "bwd") if not args.dropout else None,
                      "kernel": "fa_bwd_prep_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (the events bracket all "
                                "three)", "mean_launch_us": round(mean_s * 1e6, 3)},
     }
@@ -414,8 +442,8 @@ def main() -> int:
 
     w = attn_inputs.ALL_WORKLOADS[args.workload]
     if args.summarize_traffic:
-        text = summarize_traffic(args.summarize_traffic, w)
-        with open(TRAFFIC_FILE, "w", encoding="utf-8") as f:
+        text = summarize_traffic(args.summarize_traffic, w, args.pass_)
+        with open(TRAFFIC_FILES[args.pass_], "w", encoding="utf-8") as f:
             f.write(text)
         print(text)
         return 0
@@ -435,7 +463,7 @@ def main() -> int:
     import tiled_attention_06_amd as fa
 
     if args.traffic_probe:
-        traffic_probe(w, steps=3)
+        traffic_probe(w, steps=3, pass_=args.pass_)
         return 0
     if args.pass_ == "bwd":
         return bench_bwd(args, w)
