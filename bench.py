@@ -48,8 +48,11 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 MFMA (256 CU x 2.4 GHz x
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (bf16 causal, L=4096, D=128) and % of MFMA peak"
 _CSRC = os.path.join(ROOT, "tiled_attention_06_amd", "csrc")
-KERNEL_SOURCES = {"fwd": [os.path.join(_CSRC, f) for f in ("fa_fwd_kernel.hpp", "fa355.hip")],
-                  "bwd": [os.path.join(_CSRC, f) for f in ("fa_fwd_kernel.hpp", "fa_bwd_kernel.hpp", "fa355.hip")]}
+# the sources and the build script (its compiler flags shape the machine code)
+_BUILD = os.path.join(ROOT, "tiled_attention_06_amd", "build.py")
+KERNEL_SOURCES = {"fwd": [os.path.join(_CSRC, f) for f in ("fa_fwd_kernel.hpp", "fa355.hip")] + [_BUILD],
+                  "bwd": [os.path.join(_CSRC, f) for f in ("fa_fwd_kernel.hpp", "fa_bwd_kernel.hpp", "fa355.hip")]
+                  + [_BUILD]}
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "fa_fwd_kernel_train7b_4k_traffic.md"),
                  "bwd": os.path.join(ROOT, "profiles", "fa_bwd_kernels_train7b_4k_traffic.md")}
 

@@ -27,6 +27,11 @@ HIPCC_FLAGS = [
     "-shared",
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs where they are used by VALU code: without it the dK/dV
+    # kernel (one wave per SIMD, over 256 registers) put its score tiles in AGPRs and
+    # copied every element back (~9 VALU copies per MFMA); the other kernels'
+    # machine code is unchanged by it
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
     "-Wl,--no-undefined",  # a missing kernel stub must fail the build, not the first load
 ]
