@@ -121,3 +121,37 @@ def test_dropout_train_shape_sampled():
     bh = [(0, 0), (w.B - 1, w.H - 1)]
     ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, w.scale, True, heads=bh, dropout_p=p, seed=seed)
     compare_bwd((dq.cpu(), dk.cpu(), dv.cpu()), ref, w.dtype, "dropout train bwd", heads=bh)
+
+
+@pytest.mark.parametrize("p,seed", [(0.1, 7), (0.5, 2 ** 40 + 3), (0.9, 12345)])
+def test_dropout_masks_bit_exact(p, seed):
+    """Read each kernel's keep bits back exactly and compare them with oracle/philox.py bit for bit.
+
+    With 128 keys, D = 128, q = 0 (uniform weights 1/128, exact), v = I and dO chosen per kernel:
+      forward:  O[i, d]  > 0  iff key d is kept for row i;
+      dK/dV:    dO = I  gives  dV[j, i] > 0  iff key j is kept for row i;
+      dQ:       k = I, dO = 1 (so dP = 1) gives  dQ[i, d] > 0  iff key d is kept for row i
+                (dS = P (M − Δ) with Δ ≈ 1 < 256/T for kept keys, −P Δ < 0 for dropped ones).
+    """
+    from oracle.philox import dropout_keep
+
+    B, H, L, D = 1, 3, 128, 128
+    dt = torch.bfloat16
+    eye = torch.eye(L, dtype=dt, device=DEV).expand(B, H, L, D).contiguous()
+    q = torch.zeros(B, H, L, D, dtype=dt, device=DEV)
+    k = torch.randn(B, H, L, D, dtype=dt, device=DEV)
+    o, lse = fa.fa_fwd_dropout(q, k, eye, dropout_p=p, seed=seed)
+    ones = torch.ones(B, H, L, D, dtype=dt, device=DEV)
+    _, _, dv = fa.fa_bwd(q, k, eye, o, eye, lse, dropout_p=p, seed=seed)
+    o2, lse2 = fa.fa_fwd_dropout(q, eye, eye, dropout_p=p, seed=seed)
+    dq, _, _ = fa.fa_bwd(q, eye, eye, o2, ones, lse2, dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    for h in range(H):
+        want = dropout_keep(h, np.arange(L), np.arange(L), p, seed)        # [row, key]
+        got_fwd = (o[0, h].float().cpu().numpy() > 0)
+        got_dkdv = (dv[0, h].float().cpu().numpy() > 0).T
+        got_dq = (dq[0, h].float().cpu().numpy() > 0)
+        note(f"  head {h}: keep fraction {want.mean():.3f}")
+        assert np.array_equal(got_fwd, want), f"forward mask differs in {np.sum(got_fwd != want)} places"
+        assert np.array_equal(got_dkdv, want), f"dK/dV mask differs in {np.sum(got_dkdv != want)} places"
+        assert np.array_equal(got_dq, want), f"dQ mask differs in {np.sum(got_dq != want)} places"
