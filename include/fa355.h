@@ -228,6 +228,32 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                    int dtype, float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes,
                    fa_stream_t stream);
 
+/*
+ * fa_fwd_dropout_strided — fa_fwd_dropout on strided views (the strides of
+ * fa_fwd_strided, with its checks).
+ */
+int fa_fwd_dropout_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                           int Lk, int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                           const int64_t* o_stride, float scale, int causal, int dtype, float dropout_p,
+                           uint64_t seed, fa_stream_t stream);
+
+/*
+ * fa_bwd_strided — fa_bwd (and, with dropout_p > 0, fa_bwd_dropout) on strided
+ * views: `strides` points to 24 int64 values, the (batch, head, row) element
+ * strides of q, k, v, o, dout, dq, dk, dv in that order (each head dim
+ * contiguous), so [B, L, H, D] tensors and packed qkv / dqkv buffers are used in
+ * place.  Strides must be >= 0 with a row stride >= D (FA_ERR_STRIDE) and
+ * multiples of 8 elements (FA_ERR_ALIGN); ((L + 256) * row_stride + D) * 2 must
+ * stay below 2^32 per tensor (FA_ERR_SHAPE).  lse and the workspace stay dense.
+ * Output views (dq, dk, dv) must not overlap each other or the inputs.  NULL
+ * strides: FA_ERR_NULL.  fa_bwd and fa_bwd_dropout are this call with the dense
+ * strides.
+ */
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk, int D, const int64_t* strides,
+                   float scale, int causal, int dtype, float dropout_p, uint64_t seed, void* workspace,
+                   size_t workspace_bytes, fa_stream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);
 

@@ -50,7 +50,8 @@ def call_strided(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, Lq=64, Lk=6
 def test_header_declares_the_abi():
     assert declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
                                     "fa_bwd_workspace_size", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout",
-                                    "fa_status_string", "fa_last_hip_error", "fa_version"]
+                                    "fa_fwd_dropout_strided", "fa_bwd_strided", "fa_status_string",
+                                    "fa_last_hip_error", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -332,3 +333,39 @@ def test_dropout_entry_points_run_the_common_checks():
     assert fa.lib.fa_fwd_dropout(*P, 1, 2, 64, 64, 96, 0.125, 0, 1, 0.1, 7, None) == -3
     assert fa.lib.fa_fwd_dropout(*P, 1, 2, 65, 64, 128, 0.125, 1, 1, 0.1, 7, None) == -7
     assert fa.lib.fa_fwd_dropout(*P, 1, 2, 64, 64, 128, float("nan"), 0, 1, 0.1, 2 ** 64 - 1, None) == -6
+
+
+def call_bwd_strided(strides="blhd", B=1, H=2, Lq=300, Lk=500, D=128, ws_bytes=None, **kw):
+    """fa_bwd_strided with [B, L, H, D] strides for all eight tensors unless `strides` is a list."""
+    if strides == "blhd":
+        rows = [Lq, Lk, Lk, Lq, Lq, Lq, Lk, Lk]
+        strides = [x for L in rows for x in (L * H * D, D, H * D)]
+    arr = None if strides is None else (ctypes.c_int64 * 24)(*strides)
+    p = dict(zip(["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"], PB))
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_size(B, H, Lq)
+    a = dict(scale=0.125, causal=0, dtype=1, p=0.0)
+    a.update(kw)
+    return fa.lib.fa_bwd_strided(p["q"], p["k"], p["v"], p["o"], p["dout"], p["lse"], p["dq"], p["dk"], p["dv"],
+                                 B, H, Lq, Lk, D, None if arr is None else ctypes.cast(arr, ctypes.c_void_p),
+                                 a["scale"], a["causal"], a["dtype"], a["p"], 7, p["ws"], ws_bytes, None)
+
+
+def test_bwd_strided_checks():
+    good = [x for L in [300, 500, 500, 300, 300, 300, 500, 500] for x in (L * 2 * 128, 128, 2 * 128)]
+    assert call_bwd_strided(strides=None) == -1
+    assert call_bwd_strided(scale=float("nan")) == -6                 # valid strides reach later checks
+    for t in range(8):
+        bad = list(good)
+        bad[3 * t + 2] = 64                                           # row stride < D
+        assert call_bwd_strided(strides=bad) == -10
+        bad = list(good)
+        bad[3 * t] = -8                                               # negative batch stride
+        assert call_bwd_strided(strides=bad) == -10
+        bad = list(good)
+        bad[3 * t + 1] = 132                                          # head stride not a multiple of 8
+        assert call_bwd_strided(strides=bad) == -5
+    big = list(good)
+    big[3 * 1 + 2] = 1 << 22                                          # k rows beyond 32-bit offsets
+    assert call_bwd_strided(strides=big) == -2
+    assert call_bwd_strided(p=1.0) == -13

@@ -185,3 +185,62 @@ def test_flash_attention_autograd():
     direct = run_bwd(inp, do, True)
     for x, y in zip(got, direct):
         assert torch.equal(x, y)
+
+
+def _blhd(t):
+    """A [B, H, L, D] view of [B, L, H, D] storage holding t's values."""
+    return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_strided_matches_dense_bitwise(causal):
+    # q, k, v, o, dout and dq, dk, dv all as [B, L, H, D] views: the same bits as the dense call
+    inp = ai.make_custom(2, 3, 300, 333, 128, "bf16", causal, seed=96_001)
+    do = ai.make_dout((2, 3, 300, 128), "bf16", seed=96_002)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    dod = do.to(DEV)
+    o, lse = fa.fa_fwd(q, k, v, causal=causal)
+    ref = fa.fa_bwd(q, k, v, o, dod, lse, causal=causal)
+    qs, ks, vs, os_, ds = (_blhd(t) for t in (q, k, v, o, dod))
+    outs = [torch.full((t.shape[0], t.shape[2], t.shape[1], t.shape[3]), float("nan"), dtype=t.dtype,
+                       device=DEV).transpose(1, 2) for t in (q, k, v)]
+    got = fa.fa_bwd(qs, ks, vs, os_, ds, lse, *outs, causal=causal)
+    torch.cuda.synchronize()
+    assert not got[0].is_contiguous()
+    for a, b in zip(ref, got):
+        assert torch.equal(a.cpu(), b.cpu().contiguous())
+
+
+def test_bwd_qkvpacked_in_place():
+    # forward and backward on views of one packed qkv buffer [B, L, 3, H, D], gradients into a packed dqkv
+    B, L, H, D = 2, 257, 4, 64
+    inp = ai.make_custom(B, H, L, L, D, "fp16", True, seed=97_001)
+    do = ai.make_dout((B, H, L, D), "fp16", seed=97_002)
+    qkv = torch.stack([inp[n].transpose(1, 2) for n in ("q", "k", "v")], dim=2).contiguous().to(DEV)
+    q, k, v = (qkv[:, :, j].transpose(1, 2) for j in range(3))
+    o, lse = fa.fa_fwd(q, k, v, causal=True)
+    dqkv = torch.full_like(qkv, float("nan"))
+    dq, dk, dv = (dqkv[:, :, j].transpose(1, 2) for j in range(3))
+    fa.fa_bwd(q, k, v, o, do.to(DEV), lse, dq, dk, dv, causal=True)
+    torch.cuda.synchronize()
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, inp["scale"], True)
+    compare((dq.cpu().contiguous(), dk.cpu().contiguous(), dv.cpu().contiguous()), ref, "fp16", "bwd packed")
+
+
+def test_flash_attention_on_blhd_views():
+    # the autograd function on [B, L, H, D] tensors (as transposed views), no copies, with dropout
+    B, L, H, D = 1, 300, 2, 128
+    inp = ai.make_custom(B, H, L, L, D, "bf16", True, seed=98_001)
+    do = ai.make_dout((B, H, L, D), "bf16", seed=98_002)
+    leaves = [inp[n].transpose(1, 2).contiguous().to(DEV).requires_grad_(True) for n in ("q", "k", "v")]
+    q, k, v = (t.transpose(1, 2) for t in leaves)
+    o = fa.flash_attention(q, k, v, causal=True, dropout_p=0.15, seed=99)
+    o.backward(do.to(DEV))
+    torch.cuda.synchronize()
+    from oracle import attention_fp64
+
+    O_ref, _ = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], True, dropout_p=0.15, seed=99)
+    assert np.abs(o.detach().double().cpu().numpy() - O_ref).max() <= TOL["bf16"]
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, inp["scale"], True, dropout_p=0.15, seed=99)
+    grads = tuple(t.grad.transpose(1, 2).cpu().contiguous() for t in leaves)
+    compare(grads, ref, "bf16", "autograd views")

@@ -8,7 +8,8 @@ library is missing, importing this package raises ImportError.
 Names follow the C ABI: ``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_status_string``, ``fa_last_hip_error``,
 ``fa_version``, ``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_fwd_dropout``,
-``fa_bwd_dropout`` (also reached through ``dropout_p`` of ``fa_fwd`` / ``fa_bwd``); ``fa_fwd_qkvpacked`` is a
+``fa_bwd_dropout``, ``fa_fwd_dropout_strided``, ``fa_bwd_strided`` (reached through ``fa_fwd`` /
+``fa_bwd`` with views and ``dropout_p``); ``fa_fwd_qkvpacked`` is a
 view helper over ``fa_fwd_strided`` for a packed [B, L, 3, H, D] qkv buffer,
 ``suggest_num_splits`` a host heuristic, and ``flash_attention`` an autograd
 function whose forward is ``fa_fwd`` and whose backward is ``fa_bwd``.
@@ -57,6 +58,12 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_dropout.argtypes = [vp] * 9 + [i] * 5 + [ctypes.c_float, i, i, ctypes.c_float, ctypes.c_uint64, vp,
                                                        ctypes.c_size_t, vp]
     lib.fa_bwd_dropout.restype = i
+    lib.fa_fwd_dropout_strided.argtypes = ([vp] * 5 + [i] * 5 + [vp] * 4 +
+                                           [ctypes.c_float, i, i, ctypes.c_float, ctypes.c_uint64, vp])
+    lib.fa_fwd_dropout_strided.restype = i
+    lib.fa_bwd_strided.argtypes = ([vp] * 9 + [i] * 5 + [vp, ctypes.c_float, i, i, ctypes.c_float, ctypes.c_uint64,
+                                                         vp, ctypes.c_size_t, vp])
+    lib.fa_bwd_strided.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
@@ -170,17 +177,24 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | 
 def fa_fwd_dropout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None,
                    lse: torch.Tensor | None = None, *, causal: bool = False, scale: float | None = None,
                    dropout_p: float = 0.0, seed: int = 0, stream: torch.cuda.Stream | None = None):
-    """The C ``fa_fwd_dropout``: dense [B, H, L, D] tensors, dropout probability and 64-bit seed."""
+    """The C ``fa_fwd_dropout`` (dense tensors) or ``fa_fwd_dropout_strided`` (views): dropout probability
+    and 64-bit seed."""
     B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
-    if not all(t.is_contiguous() for t in (q, k, v, o)):
-        raise ValueError("fa_fwd_dropout takes dense [B, H, L, D] tensors")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    code = lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Lq, Lk,
-                              D, float(scale), 1 if causal else 0, _DTYPES[q.dtype], float(dropout_p),
-                              int(seed) & 0xFFFFFFFFFFFFFFFF, stream.cuda_stream)
+    seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    if all(t.is_contiguous() for t in (q, k, v, o)):
+        code = lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Lq,
+                                  Lk, D, float(scale), 1 if causal else 0, _DTYPES[q.dtype], float(dropout_p), seed,
+                                  stream.cuda_stream)
+    else:
+        st = [(ctypes.c_int64 * 3)(*t.stride()[:3]) for t in (q, k, v, o)]
+        code = lib.fa_fwd_dropout_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                          B, H, Lq, Lk, D, *[ctypes.cast(s_, ctypes.c_void_p) for s_ in st],
+                                          float(scale), 1 if causal else 0, _DTYPES[q.dtype], float(dropout_p),
+                                          seed, stream.cuda_stream)
     if code != 0:
         raise FaError(code)
     return o, lse
@@ -261,10 +275,12 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, d
            seed: int = 0):
     """Enqueue the attention backward pass (the C ``fa_bwd``): gradients of o = fa_fwd(q, k, v) for dout.
 
-    q, o, dout: [B, H, Lq, D]; k, v: [B, H, Lk, D]; lse: [B, H, Lq] float32 (fa_fwd's outputs o and lse
-    for the same q, k, v, scale and causal flag).  All dense (contiguous).  dq, dk, dv are allocated when
-    not given; ``workspace`` (at least ``fa_bwd_workspace_size`` bytes) likewise.  With ``dropout_p`` > 0
-    the call is ``fa_bwd_dropout`` (same probability and seed as the forward pass).  Returns (dq, dk, dv).
+    q, o, dout: [B, H, Lq, D]; k, v: [B, H, Lk, D]; lse: [B, H, Lq] float32 dense (fa_fwd's outputs o and
+    lse for the same q, k, v, scale and causal flag).  Tensors may be views of any strides with a
+    contiguous head dim (dense ones go through ``fa_bwd`` / ``fa_bwd_dropout``, others through
+    ``fa_bwd_strided``).  dq, dk, dv (q's, k's, v's shapes; views allowed) are allocated dense when not
+    given; ``workspace`` (at least ``fa_bwd_workspace_size`` bytes) likewise.  ``dropout_p`` and ``seed``
+    must be those of the forward pass.  Returns (dq, dk, dv).
     """
     B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
     if tuple(dout.shape) != tuple(q.shape) or dout.dtype != q.dtype or dout.device != q.device:
@@ -275,9 +291,11 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, d
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if tuple(t.shape) != tuple(ref.shape) or t.dtype != q.dtype or t.device != q.device:
             raise ValueError(f"{name} must be a tensor of {name[1:]}'s shape, dtype and device")
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
-        if not t.is_contiguous():
-            raise ValueError(f"fa_bwd takes dense [B, H, L, D] tensors: {name} is not contiguous")
+    tensors = (q, k, v, o, dout, dq, dk, dv)
+    for name, t in zip(("q", "k", "v", "o", "dout", "dq", "dk", "dv"), tensors):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}: the head dim must be contiguous (stride 1)")
+    dense = all(t.is_contiguous() for t in tensors)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if stream is None:
@@ -285,7 +303,15 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, d
     need = fa_bwd_workspace_size(B, H, Lq)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if dropout_p:
+    if not dense:
+        st = (ctypes.c_int64 * 24)(*[x for t in tensors for x in t.stride()[:3]])
+        code = lib.fa_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D,
+                                  ctypes.cast(st, ctypes.c_void_p), float(scale), 1 if causal else 0,
+                                  _DTYPES[q.dtype], float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  stream.cuda_stream)
+    elif dropout_p:
         code = lib.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                                   lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D,
                                   float(scale), 1 if causal else 0, _DTYPES[q.dtype], float(dropout_p),
@@ -304,7 +330,7 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, d
 class _FlashAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, causal, scale, dropout_p, seed):
-        q, k, v = (t.contiguous() for t in (q, k, v))
+        # views are used in place (a contiguous head dim is all the kernels need)
         o, lse = fa_fwd(q, k, v, causal=causal, scale=scale, dropout_p=dropout_p, seed=seed)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.causal, ctx.scale, ctx.dropout_p, ctx.seed = causal, scale, dropout_p, seed
@@ -313,8 +339,10 @@ class _FlashAttention(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = fa_bwd(q, k, v, o, do.contiguous(), lse, causal=ctx.causal, scale=ctx.scale,
-                            dropout_p=ctx.dropout_p, seed=ctx.seed)
+        if do.stride(3) != 1:
+            do = do.contiguous()
+        dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale, dropout_p=ctx.dropout_p,
+                            seed=ctx.seed)
         return dq, dk, dv, None, None, None, None
 
 

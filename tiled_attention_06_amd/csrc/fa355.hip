@@ -197,16 +197,29 @@ int dispatch_bwd(const fa355::BwdParams& p, int dtype, bool causal, hipStream_t 
   return causal ? launch_bwd<D, fa355::DT_F16, true, DROP>(p, s) : launch_bwd<D, fa355::DT_F16, false, DROP>(p, s);
 }
 
+// strides: 24 values, (batch, head, row) element strides of q, k, v, o, dout, dq,
+// dk, dv in that order; NULL means dense [B, H, L, D] for all eight.
 int bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
-        void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal, int dtype, void* ws,
-        size_t ws_size, fa_stream_t stream, float dropout_p = 0.0f, uint64_t seed = 0) {
+        void* dk, void* dv, int B, int H, int Lq, int Lk, int D, const int64_t* strides, float scale, int causal,
+        int dtype, void* ws, size_t ws_size, fa_stream_t stream, float dropout_p = 0.0f, uint64_t seed = 0) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !ws) return FA_ERR_NULL;
   if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  // rows of q, o, dout, dq have Lq entries; rows of k, v, dk, dv have Lk
+  const int64_t len[8] = {Lq, Lk, Lk, Lq, Lq, Lq, Lk, Lk};
+  int64_t st[8][3];
+  for (int i = 0; i < 8; ++i) {
+    st[i][0] = strides ? strides[3 * i] : (int64_t)H * len[i] * D;
+    st[i][1] = strides ? strides[3 * i + 1] : len[i] * D;
+    st[i][2] = strides ? strides[3 * i + 2] : D;
+    if (st[i][0] < 0 || st[i][1] < 0 || st[i][2] < D) return FA_ERR_STRIDE;
+  }
   const void* p16[8] = {q, k, v, o, dout, dq, dk, dv};
   for (int i = 0; i < 8; ++i)
     if (!aligned(p16[i], 16)) return FA_ERR_ALIGN;
+  for (int i = 0; i < 8; ++i)  // every row starts on a 16-byte boundary
+    if (st[i][0] % 8 || st[i][1] % 8 || st[i][2] % 8) return FA_ERR_ALIGN;
   if (!aligned(lse, 4) || !aligned(ws, 256)) return FA_ERR_ALIGN;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (causal && Lq > Lk) return FA_ERR_CAUSAL_SHAPE;
@@ -214,7 +227,8 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
   if (drop_t < 0) return FA_ERR_DROPOUT;
   if (ws_size < bwd_ws_bytes(B, H, Lq)) return FA_ERR_WORKSPACE;
   // one head's slab plus a tile of padding in 32-bit byte offsets
-  if (((int64_t)Lq + 256) * D * 2 >= (1ll << 32) || ((int64_t)Lk + 256) * D * 2 >= (1ll << 32)) return FA_ERR_SHAPE;
+  for (int i = 0; i < 8; ++i)
+    if (((len[i] + 256) * st[i][2] + D) * 2 >= (1ll << 32)) return FA_ERR_SHAPE;
   const int64_t n_qt = ((int64_t)Lq + kBwdDqRows - 1) / kBwdDqRows;
   const int64_t n_kt = ((int64_t)Lk + kBwdKvKeys - 1) / kBwdKvKeys;
   if ((int64_t)B * H >= (1ll << 31) || (int64_t)B * H * n_qt >= (1ll << 22) || (int64_t)B * H * n_kt >= (1ll << 22))
@@ -236,6 +250,12 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
   p.Lq4 = (int)lq4(Lq);
   p.Lk = Lk;
   p.bh = (int)((int64_t)B * H);
+  p.H = H;
+  for (int i = 0; i < 8; ++i) {
+    p.sb[i] = st[i][0];
+    p.sh[i] = st[i][1];
+    p.sl[i] = (int)st[i][2];
+  }
   p.kv_off = Lk - Lq;
   p.n_qt = (int)n_qt;
   p.n_kt = (int)n_kt;
@@ -293,8 +313,17 @@ size_t fa_bwd_workspace_size(int B, int H, int Lq) {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
            void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, fa_stream_t stream) {
-  return bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Lq, Lk, D, scale, causal, dtype, workspace, workspace_bytes,
-             stream);
+  return bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Lq, Lk, D, nullptr, scale, causal, dtype, workspace,
+             workspace_bytes, stream);
+}
+
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk, int D, const int64_t* strides,
+                   float scale, int causal, int dtype, float dropout_p, uint64_t seed, void* workspace,
+                   size_t workspace_bytes, fa_stream_t stream) {
+  if (!strides) return FA_ERR_NULL;
+  return bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Lq, Lk, D, strides, scale, causal, dtype, workspace,
+             workspace_bytes, stream, dropout_p, seed);
 }
 
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
@@ -305,12 +334,20 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
              seed);
 }
 
+int fa_fwd_dropout_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                           int Lk, int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                           const int64_t* o_stride, float scale, int causal, int dtype, float dropout_p,
+                           uint64_t seed, fa_stream_t stream) {
+  return fwd(q, k, v, o, lse, B, H, Lq, Lk, D, q_stride, k_stride, v_stride, o_stride, scale, causal, dtype, 1,
+             nullptr, 0, stream, dropout_p, seed);
+}
+
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                    void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk, int D, float scale, int causal,
                    int dtype, float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes,
                    fa_stream_t stream) {
-  return bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Lq, Lk, D, scale, causal, dtype, workspace, workspace_bytes,
-             stream, dropout_p, seed);
+  return bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Lq, Lk, D, nullptr, scale, causal, dtype, workspace,
+             workspace_bytes, stream, dropout_p, seed);
 }
 
 const char* fa_status_string(int status) {

@@ -54,6 +54,11 @@ struct BwdParams {
   int Lq, Lk;
   int Lq4;            // Lq rounded up to a multiple of 4: 16-byte groups of rows never straddle the end
   int bh;             // B*H
+  int H;              // heads (b = bh / H, h = bh % H)
+  // element strides of batch, head and row of q, k, v, o, dout, dq, dk, dv (in
+  // that order, indices T_Q .. T_DV); the head dim is contiguous
+  int64_t sb[8], sh[8];
+  int sl[8];
   int kv_off;         // causal: key position of query row 0 (Lk - Lq >= 0)
   int n_qt;           // query tiles of 256 rows per head (dq kernel)
   int n_kt;           // key tiles of 128 keys per head (dkdv kernel)
@@ -66,6 +71,20 @@ struct BwdParams {
   uint32_t drop_t, seed_lo, seed_hi;
   float drop_scale;
 };
+
+enum { T_Q = 0, T_K, T_V, T_O, T_DO, T_DQ, T_DK, T_DV };
+
+// Start of tensor T's (batch, head) slab; its rows are sl[T] elements apart.
+template <typename Ptr>
+__device__ __forceinline__ Ptr bwd_slab(Ptr base, const BwdParams& p, int T, int bh) {
+  const int b = bh / p.H, h = bh - b * p.H;
+  return (Ptr)((const char*)base + ((int64_t)b * p.sb[T] + (int64_t)h * p.sh[T]) * 2);
+}
+// Bytes from a slab's start to the end of its last row of `rows` (the buffer range)
+template <int D>
+__device__ __forceinline__ uint32_t bwd_end(const BwdParams& p, int T, int rows) {
+  return (uint32_t)(((int64_t)(rows - 1) * p.sl[T] + D) * 2);
+}
 
 // The two 16-bit values of a dword as fp32 (exact), low half first.
 template <int DT>
@@ -88,11 +107,13 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
   const int64_t total = (int64_t)p.bh * p.Lq4;
   const int64_t bh = w / p.Lq4, i = w - bh * p.Lq4;
   const bool real = w < total && i < p.Lq;
-  const int64_t r = bh * p.Lq + i;  // the row in o, dout and lse
+  const int64_t r = bh * p.Lq + i;  // the row in lse
   float acc = 0.f;
   if (real) {
-    const u32x4 a = *(const u32x4*)((const char*)p.o + (r * D + c0) * 2);
-    const u32x4 b = *(const u32x4*)((const char*)p.dout + (r * D + c0) * 2);
+    const char* orow = bwd_slab((const char*)p.o, p, T_O, (int)bh) + (i * p.sl[T_O] + c0) * 2;
+    const char* drow = bwd_slab((const char*)p.dout, p, T_DO, (int)bh) + (i * p.sl[T_DO] + c0) * 2;
+    const u32x4 a = *(const u32x4*)orow;
+    const u32x4 b = *(const u32x4*)drow;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float2 x = unpack2<DT>(a[e]), y = unpack2<DT>(b[e]);
@@ -117,18 +138,19 @@ struct BwdCopy {
   using G = Geo<D>;
   static constexpr int NCH = G::NCH, NBLK = G::NBLK, CPW = NBLK / NW;
   static_assert(NBLK % NW == 0, "copy layout");
-  uint32_t lane_src, step;  // per-lane source offset within a tile, offset between a wave's copies
+  uint32_t lane_src, step, row_bytes;  // per-lane source offset in a tile, offset between a wave's copies
   int wave;
-  __device__ __forceinline__ BwdCopy(int wave_, int lane) : wave(wave_) {
+  __device__ __forceinline__ BwdCopy(int wave_, int lane, int row_stride) : wave(wave_) {
+    row_bytes = (uint32_t)row_stride * 2u;
     const int lrow = wave_ + NBLK * (lane / NCH), lchunk = 16 * (lane % NCH);
-    lane_src = (uint32_t)(lrow * D * 2 + lchunk);
-    step = (uint32_t)(NW * D * 2);
+    lane_src = (uint32_t)lrow * row_bytes + (uint32_t)lchunk;
+    step = (uint32_t)NW * row_bytes;
   }
-  // rows [64·tile, 64·tile + 64) of a slab of `rows` rows; rows past the end read 0
+  // rows [64·tile, 64·tile + 64) of a slab whose last row ends `end` bytes after
+  // its start; rows past the end read 0
   template <int BS>
-  __device__ __forceinline__ void copy(const char* slab, int rows, int tile, unsigned char* dst) const {
-    const uint32_t off = (uint32_t)tile * 64u * D * 2u;
-    const uint32_t end = (uint32_t)rows * D * 2u;
+  __device__ __forceinline__ void copy(const char* slab, uint32_t end, int tile, unsigned char* dst) const {
+    const uint32_t off = (uint32_t)tile * 64u * row_bytes;
     const uint64_t base = (uint64_t)(uintptr_t)(slab + off);
     const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xffffu)),
@@ -172,21 +194,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int i0 = qt * BR, i0w = i0 + 32 * wave;
   const int off = CAUSAL ? p.kv_off : 0;
 
-  const char* const qslab = (const char*)p.q + (int64_t)bh * Lq * D * 2;
-  const char* const doslab = (const char*)p.dout + (int64_t)bh * Lq * D * 2;
-  const char* const kslab = (const char*)p.k + (int64_t)bh * Lk * D * 2;
-  const char* const vslab = (const char*)p.v + (int64_t)bh * Lk * D * 2;
-  const auto qrs = make_rsrc(qslab, (uint32_t)Lq * D * 2);
-  const auto dors = make_rsrc(doslab, (uint32_t)Lq * D * 2);
+  const char* const qslab = bwd_slab((const char*)p.q, p, T_Q, bh);
+  const char* const doslab = bwd_slab((const char*)p.dout, p, T_DO, bh);
+  const char* const kslab = bwd_slab((const char*)p.k, p, T_K, bh);
+  const char* const vslab = bwd_slab((const char*)p.v, p, T_V, bh);
+  const auto qrs = make_rsrc(qslab, bwd_end<D>(p, T_Q, Lq));
+  const auto dors = make_rsrc(doslab, bwd_end<D>(p, T_DO, Lq));
+  const uint32_t end_k = bwd_end<D>(p, T_K, Lk), end_v = bwd_end<D>(p, T_V, Lk);
 
   int n_kv = (Lk + BC - 1) / BC;
   if constexpr (CAUSAL) n_kv = min(n_kv, (min(i0 + BR, Lq) - 1 + off) / BC + 1);
 
-  const BwdCopy<D, NW> cp(wave, lane);
+  const BwdCopy<D, NW> cpk(wave, lane, p.sl[T_K]), cpv(wave, lane, p.sl[T_V]);
   auto copies = [&](int t, int st) {
-    cp.template copy<KBS>(kslab, Lk, t, st ? kr1 : kr0);
-    cp.template copy<VBS>(kslab, Lk, t, st ? kt1 : kt0);
-    cp.template copy<KBS>(vslab, Lk, t, st ? vr1 : vr0);
+    cpk.template copy<KBS>(kslab, end_k, t, st ? kr1 : kr0);
+    cpk.template copy<VBS>(kslab, end_k, t, st ? kt1 : kt0);
+    cpv.template copy<KBS>(vslab, end_v, t, st ? vr1 : vr0);
   };
   if (n_kv > 0) copies(0, 0);
 
@@ -196,8 +219,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   u32x4 qr[KS], dr[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    qr[s] = buf_load16(qrs, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2);
-    dr[s] = buf_load16(dors, (uint32_t)(qrow * D + 16 * s + 8 * g) * 2);
+    qr[s] = buf_load16(qrs, (uint32_t)(qrow * p.sl[T_Q] + 16 * s + 8 * g) * 2);
+    dr[s] = buf_load16(dors, (uint32_t)(qrow * p.sl[T_DO] + 16 * s + 8 * g) * 2);
   }
   const bool row_ok = qrow < Lq;
   const float lse2 = row_ok ? p.ws_lse2[(int64_t)bh * p.Lq4 + qrow] : 0.f;
@@ -293,7 +316,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // epilogue: dQ = scale·dQᵀ; lane holds dims 32nb + 8(r/4) + 4g + r%4 of row qrow
-  const auto ors = make_rsrc((char*)p.dq + (int64_t)bh * Lq * D * 2, (uint32_t)Lq * D * 2);
+  const auto ors = make_rsrc(bwd_slab((char*)p.dq, p, T_DQ, bh), bwd_end<D>(p, T_DQ, Lq));
   const float sc = p.scale;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -302,7 +325,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int d0 = 32 * nb + 8 * q4 + 4 * g;
       const u32x2 w = {pack2<DT>(dq[nb][4 * q4] * sc, dq[nb][4 * q4 + 1] * sc),
                        pack2<DT>(dq[nb][4 * q4 + 2] * sc, dq[nb][4 * q4 + 3] * sc)};
-      buf_store8(ors, (uint32_t)(qrow * D + d0) * 2, w);  // rows >= Lq are dropped
+      buf_store8(ors, (uint32_t)(qrow * p.sl[T_DQ] + d0) * 2, w);  // rows >= Lq are dropped
     }
 }
 
@@ -334,18 +357,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int j0 = kt * BKV, j0w = j0 + 32 * wave;
   const int off = CAUSAL ? p.kv_off : 0;
 
-  const char* const qslab = (const char*)p.q + (int64_t)bh * Lq * D * 2;
-  const char* const doslab = (const char*)p.dout + (int64_t)bh * Lq * D * 2;
-  const char* const kslab = (const char*)p.k + (int64_t)bh * Lk * D * 2;
-  const char* const vslab = (const char*)p.v + (int64_t)bh * Lk * D * 2;
-  const auto krs = make_rsrc(kslab, (uint32_t)Lk * D * 2);
-  const auto vrs = make_rsrc(vslab, (uint32_t)Lk * D * 2);
+  const char* const qslab = bwd_slab((const char*)p.q, p, T_Q, bh);
+  const char* const doslab = bwd_slab((const char*)p.dout, p, T_DO, bh);
+  const char* const kslab = bwd_slab((const char*)p.k, p, T_K, bh);
+  const char* const vslab = bwd_slab((const char*)p.v, p, T_V, bh);
+  const auto krs = make_rsrc(kslab, bwd_end<D>(p, T_K, Lk));
+  const auto vrs = make_rsrc(vslab, bwd_end<D>(p, T_V, Lk));
+  const uint32_t end_q = bwd_end<D>(p, T_Q, Lq), end_do = bwd_end<D>(p, T_DO, Lq);
 
   // query tiles that see any key of this workgroup: rows i >= j0 - off (causal)
   const int n_q = (Lq + BQ - 1) / BQ;
   const int t_b = CAUSAL ? max(0, j0 - off) / BQ : 0;
 
-  const BwdCopy<D, NW> cp(wave, lane);
+  const BwdCopy<D, NW> cpq(wave, lane, p.sl[T_Q]), cpo(wave, lane, p.sl[T_DO]);
   // row statistics of tile t: rows past the padded end read 0
   auto copy_stats = [&](const float* base, int t, float* dst) {
     const uint64_t a = (uint64_t)(uintptr_t)(base + (int64_t)bh * p.Lq4 + (int64_t)t * BQ);
@@ -356,10 +380,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     dma16(rs, (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(dst)), (uint32_t)(16 * lane));
   };
   auto copies = [&](int t, int st) {
-    cp.template copy<KBS>(qslab, Lq, t, st ? qr1 : qr0);
-    cp.template copy<VBS>(qslab, Lq, t, st ? qt1 : qt0);
-    cp.template copy<KBS>(doslab, Lq, t, st ? or1 : or0);
-    cp.template copy<VBS>(doslab, Lq, t, st ? ot1 : ot0);
+    cpq.template copy<KBS>(qslab, end_q, t, st ? qr1 : qr0);
+    cpq.template copy<VBS>(qslab, end_q, t, st ? qt1 : qt0);
+    cpo.template copy<KBS>(doslab, end_do, t, st ? or1 : or0);
+    cpo.template copy<VBS>(doslab, end_do, t, st ? ot1 : ot0);
     if (wave == 0) copy_stats(p.ws_lse2, t, st ? ls1 : ls0);
     if (wave == 1) copy_stats(p.ws_delta, t, st ? de1 : de0);
   };
@@ -371,8 +395,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   u32x4 kr[KS], vr[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    kr[s] = buf_load16(krs, (uint32_t)(key * D + 16 * s + 8 * g) * 2);
-    vr[s] = buf_load16(vrs, (uint32_t)(key * D + 16 * s + 8 * g) * 2);
+    kr[s] = buf_load16(krs, (uint32_t)(key * p.sl[T_K] + 16 * s + 8 * g) * 2);
+    vr[s] = buf_load16(vrs, (uint32_t)(key * p.sl[T_V] + 16 * s + 8 * g) * 2);
   }
   const float c = p.c;
 
@@ -536,8 +560,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // epilogue: lane holds dims 32nb + 8(r/4) + 4g + r%4 of key `key`
-  const auto dkrs = make_rsrc((char*)p.dk + (int64_t)bh * Lk * D * 2, (uint32_t)Lk * D * 2);
-  const auto dvrs = make_rsrc((char*)p.dv + (int64_t)bh * Lk * D * 2, (uint32_t)Lk * D * 2);
+  const auto dkrs = make_rsrc(bwd_slab((char*)p.dk, p, T_DK, bh), bwd_end<D>(p, T_DK, Lk));
+  const auto dvrs = make_rsrc(bwd_slab((char*)p.dv, p, T_DV, bh), bwd_end<D>(p, T_DV, Lk));
   const float sc = p.scale;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -548,8 +572,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         pack2<DT>(dk[nb][4 * q4 + 2] * sc, dk[nb][4 * q4 + 3] * sc)};
       const u32x2 wv = {pack2<DT>(dv[nb][4 * q4], dv[nb][4 * q4 + 1]),
                         pack2<DT>(dv[nb][4 * q4 + 2], dv[nb][4 * q4 + 3])};
-      buf_store8(dkrs, (uint32_t)(key * D + d0) * 2, wk);  // keys >= Lk are dropped
-      buf_store8(dvrs, (uint32_t)(key * D + d0) * 2, wv);
+      buf_store8(dkrs, (uint32_t)(key * p.sl[T_DK] + d0) * 2, wk);  // keys >= Lk are dropped
+      buf_store8(dvrs, (uint32_t)(key * p.sl[T_DV] + d0) * 2, wv);
     }
 }
 
