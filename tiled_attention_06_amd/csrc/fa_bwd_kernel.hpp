@@ -261,21 +261,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const bool need_mask = (CAUSAL && j0 + BC - 1 > i0w + off) || (j0 + BC > Lk);
       const int lim_tail = Lk - j0 - 4 * g;
       const int lim = CAUSAL ? min(qrow + off - j0 - 4 * g + 1, lim_tail) : lim_tail;
+      // dropout words of the tile (blocks x = 4kb + 2h + a: keys 32kb + 16h + 8a + 4g + 0..3
+      // of row qrow; lane j of a quad computes blocks 2j, 2j + 1, the quad exchanges words)
+      uint32_t words[8];
+      if constexpr (DROP) {
+        const int j = lane & 3;
+        u32x4 mine[2];
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const int x = 2 * j + sl, kb = x >> 2, h = (x >> 1) & 1, a = x & 1;
+          mine[sl] = drop_block((j0 + 32 * kb + 16 * h + 8 * a + 4 * g) >> 2, qrow >> 2, bh, p.seed_lo, p.seed_hi);
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) words[x] = quad_word(mine[x & 1], x >> 1, j);
+      }
       u32x4 db[KB][2];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          // dropout bits of registers 8h..8h+7 (keys 32kb + 16h + 8a + 4g + 0..3 of row qrow)
+          // dropout words of registers 8h..8h+7
           uint32_t dwd[2] = {0u, 0u};
           if constexpr (DROP) {
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-              const u32x4 w4 = drop_block((j0 + 32 * kb + 16 * h + 8 * a + 4 * g) >> 2, qrow >> 2, bh, p.seed_lo,
-                                          p.seed_hi);
-              const int wi = qrow & 3;
-              dwd[a] = wi == 0 ? w4[0] : wi == 1 ? w4[1] : wi == 2 ? w4[2] : w4[3];
-            }
+            dwd[0] = words[4 * kb + 2 * h];
+            dwd[1] = words[4 * kb + 2 * h + 1];
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -461,11 +470,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       de[a] = *(const f32x4*)(deb + 32 * qb + 8 * a + 4 * g);
     }
   };
-  auto drop_words = [&](int qb, int h, int a, int i0) -> u32x4 {
-    if constexpr (DROP)
-      return drop_block(key >> 2, (i0 + 32 * qb + 16 * h + 8 * a + 4 * g) >> 2, bh, p.seed_lo, p.seed_hi);
-    else
-      return u32x4{};
+  // Dropout blocks of half qb: blocks x = 2h + a cover rows i0 + 32qb + 16h + 8a + 4g +
+  // 0..3 of this lane's key.  The four lanes of a quad share the key block, so lane
+  // j computes block j and the quad exchanges all four words of each block.
+  auto drop_half = [&](int qb, int i0, u32x4 (&blk)[4]) {
+    const int j = lane & 3, h = j >> 1, a = j & 1;
+    const u32x4 mine = drop_block(key >> 2, (i0 + 32 * qb + 16 * h + 8 * a + 4 * g) >> 2, bh, p.seed_lo, p.seed_hi);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      blk[x] = u32x4{quad_bcast(mine[0], x), quad_bcast(mine[1], x), quad_bcast(mine[2], x), quad_bcast(mine[3], x)};
   };
   // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS for register half h, dims block nb of half qb
   auto grad_mfma = [&](int qb, int h, int nb, const u32x4 (&pb)[2], const u32x4 (&db)[2],
@@ -500,7 +513,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     {
       f32x4 ls[4], de[4];
       load_stats(0, lsb, deb, ls, de);
-      u32x4 dw{};
+      u32x4 blk[4];
+      if constexpr (DROP) drop_half(0, i0, blk);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         S1 = mfma32<DT>(lds_read16(qrb + k_off + row_off(32, KBS) + 32 * s), kr[s], S1);
@@ -508,8 +522,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int j = 0; j < PPS; ++j) {
           const int pr = s * PPS + j, h = pr >> 2, e = pr & 3;
-          if ((e & 1) == 0) dw = drop_words(0, h, e >> 1, i0);
-          valu_pair(MASK, 0, h, e, i0, S0, dP0, ls, de, dw, pb0, db0);
+          valu_pair(MASK, 0, h, e, i0, S0, dP0, ls, de, blk[2 * h + (e >> 1)], pb0, db0);
         }
         if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
       }
@@ -517,15 +530,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     {
       f32x4 ls[4], de[4];
       load_stats(1, lsb, deb, ls, de);
-      u32x4 dw{};
+      u32x4 blk[4];
+      if constexpr (DROP) drop_half(1, i0, blk);
 #pragma unroll
       for (int st = 0; st < GSTEPS; ++st) {
         grad_mfma(0, st / NB, st % NB, pb0, db0, qtb, otb);
 #pragma unroll
         for (int j = 0; j < PPG; ++j) {
           const int pr = st * PPG + j, h = pr >> 2, e = pr & 3;
-          if ((e & 1) == 0) dw = drop_words(1, h, e >> 1, i0);
-          valu_pair(MASK, 1, h, e, i0, S1, dP1, ls, de, dw, pb1, db1);
+          valu_pair(MASK, 1, h, e, i0, S1, dP1, ls, de, blk[2 * h + (e >> 1)], pb1, db1);
         }
         if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
       }

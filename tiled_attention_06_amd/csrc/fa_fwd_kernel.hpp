@@ -137,6 +137,27 @@ __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2,
 __device__ __forceinline__ u32x4 drop_block(int key4, int row4, int bh, uint32_t k0, uint32_t k1) {
   return philox10((uint32_t)key4, (uint32_t)row4, (uint32_t)bh, 0u, k0, k1);
 }
+// Word w (the same register in every lane) of lane s of each quad of lanes
+// (quad_perm(s, s, s, s); s is a constant wherever the callers are unrolled).
+template <int S>
+__device__ __forceinline__ uint32_t quad_bcast_c(uint32_t w) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, S * 0x55, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t w, int s) {
+  switch (s) {
+    case 0: return quad_bcast_c<0>(w);
+    case 1: return quad_bcast_c<1>(w);
+    case 2: return quad_bcast_c<2>(w);
+    default: return quad_bcast_c<3>(w);
+  }
+}
+// Word j of lane s's block x, for lane j of each quad (j = lane & 3)
+__device__ __forceinline__ uint32_t quad_word(const u32x4& x, int s, int j) {
+  const uint32_t w0 = quad_bcast(x[0], s), w1 = quad_bcast(x[1], s), w2 = quad_bcast(x[2], s),
+                 w3 = quad_bcast(x[3], s);
+  return j == 0 ? w0 : j == 1 ? w1 : j == 2 ? w2 : w3;
+}
+
 // 16-bit lane masks of the kept weights of word w's bytes b0 and b0+1
 __device__ __forceinline__ uint32_t keep_pair(uint32_t w, int b0, uint32_t T) {
   const uint32_t lo = (w >> (8 * b0)) & 0xffu, hi = (w >> (8 * b0 + 8)) & 0xffu;
@@ -517,9 +538,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // With DROP, the weights that multiply V are masked by the dropout bits of
   // their (row, key); the sums stay those of all weights (dropout acts on the
   // normalised weights, and LSE is that of the scores).
+  // Dropout words of a tile: the lane needs, for blocks x = 4kb + 2h + a (keys
+  // 32kb + 16h + 8a + 4g + 0..3 of its row), word row % 4.  The four lanes of a
+  // quad share the row block, so lane j computes blocks 2j and 2j + 1 and the
+  // quad exchanges words (one Philox call per four elements becomes one per 16).
+  auto drop_tile = [&](int t, uint32_t (&words)[8]) {
+    const int lane_d = opaque(tid) & 63;
+    const int row_d = i0w + (lane_d & 31), g_d = lane_d >> 5, j = lane_d & 3;
+    u32x4 mine[2];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int x = 2 * j + sl, kb = x >> 2, h = (x >> 1) & 1, a = x & 1;
+      mine[sl] = drop_block((t * BC + 32 * kb + 16 * h + 8 * a + 4 * g_d) >> 2, row_d >> 2, bh, p.seed_lo,
+                            p.seed_hi);
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) words[x] = quad_word(mine[x & 1], x >> 1, j);
+  };
   auto make_p = [&](const f32x16(&S)[KB], u32x4(&pb)[KB][2], int t) {
     const float mb = m_run;
     float sf = 0.f, sr = 0.f;
+    uint32_t words[8];
+    if constexpr (DROP) drop_tile(t, words);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -527,14 +567,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // keys of registers 8h..8h+7: 32kb + 16h + 4g + {0..3} and + 8 + 4g + {0..3}
         u32x4 dw[2];
         if constexpr (DROP) {
-          const int lane_d = opaque(tid) & 63;
-          const int row_d = i0w + (lane_d & 31), g_d = lane_d >> 5;
 #pragma unroll
           for (int a = 0; a < 2; ++a) {
-            const u32x4 w4 = drop_block((t * BC + 32 * kb + 16 * h + 8 * a + 4 * g_d) >> 2, row_d >> 2, bh,
-                                        p.seed_lo, p.seed_hi);
-            const int wi = row_d & 3;
-            const uint32_t w = wi == 0 ? w4[0] : wi == 1 ? w4[1] : wi == 2 ? w4[2] : w4[3];
+            const uint32_t w = words[4 * kb + 2 * h + a];
             dw[a] = u32x4{keep_pair(w, 0, p.drop_t), keep_pair(w, 2, p.drop_t), 0u, 0u};
           }
         }
