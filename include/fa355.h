@@ -62,7 +62,7 @@ typedef enum {
   FA_ERR_DEVICE = -8,       /* the current device has no gfx950 code object for the kernel       */
   FA_ERR_LAUNCH = -9,       /* the kernel launch failed (HIP code in fa_last_hip_error())        */
   FA_ERR_STRIDE = -10,      /* fa_fwd_strided: a stride < 0, or a row stride < D                 */
-  FA_ERR_SPLITS = -11,      /* fa_fwd_splitkv: num_splits outside 1..64                          */
+  FA_ERR_SPLITS = -11,      /* fa_fwd_splitkv: num_splits outside 1..256                         */
   FA_ERR_WORKSPACE = -12,   /* fa_fwd_splitkv / fa_bwd: workspace smaller than its size query    */
   FA_ERR_DROPOUT = -13      /* dropout probability outside [0, 1), or round((1-p)*256) == 0      */
 } fa_status;
@@ -135,7 +135,7 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
  * one pass up to fp32 rounding.  This fills the GPU when B*H*ceil(Lq/256) is
  * small; it is also the merge a multi-GPU split of the keys would use.
  *
- *   num_splits        1..64 (FA_ERR_SPLITS otherwise); 1 is fa_fwd_strided and
+ *   num_splits        1..256 (FA_ERR_SPLITS otherwise); 1 is fa_fwd_strided and
  *                     ignores the workspace.
  *   workspace         device memory of at least
  *                     fa_fwd_splitkv_workspace_size(B, H, Lq, D, num_splits)

@@ -228,11 +228,11 @@ def test_splitkv_workspace_size():
     assert fa.fa_fwd_splitkv_workspace_size(2, 3, 100, 128, 4) == 4 * 6 * 100 * (128 + 4) * 4
     assert fa.fa_fwd_splitkv_workspace_size(1, 1, 7, 64, 3) == 3 * 7 * (64 + 4) * 4
     assert fa.fa_fwd_splitkv_workspace_size(1, 1, 7, 64, 1) == 0
-    for bad in [(0, 1, 7, 64, 2), (1, 1, 7, 96, 2), (1, 1, 7, 64, 0), (1, 1, 7, 64, 65), (1, 0, 7, 64, 2)]:
+    for bad in [(0, 1, 7, 64, 2), (1, 1, 7, 96, 2), (1, 1, 7, 64, 0), (1, 1, 7, 64, 257), (1, 0, 7, 64, 2)]:
         assert fa.fa_fwd_splitkv_workspace_size(*bad) == 0
 
 
-@pytest.mark.parametrize("splits", [0, -1, 65, 1000])
+@pytest.mark.parametrize("splits", [0, -1, 257, 1000])
 def test_splitkv_split_count(splits):
     assert call_split(splits=splits, ws_bytes=1 << 40) == -11
 
@@ -260,7 +260,8 @@ def test_suggest_num_splits():
     assert fa.suggest_num_splits(2, 32, 512, 8192, 128, True) == 2         # 128 workgroups
     assert fa.suggest_num_splits(1, 32, 1024, 1024, 64, True) == 1         # 8 tiles on average
     assert fa.suggest_num_splits(1, 1, 128, 128, 64, False) == 1           # too few keys to split
-    assert 1 <= fa.suggest_num_splits(1, 2, 256, 65536, 128, False) <= 64
+    assert 1 <= fa.suggest_num_splits(1, 2, 256, 65536, 128, False) <= 256
+    assert fa.suggest_num_splits(1, 1, 4, 1_000_003, 128, False) == 256      # one query tile, long cache
 
 
 # ------------------------------------------------------------------------------------------

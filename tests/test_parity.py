@@ -413,3 +413,22 @@ def test_split_workload(name):
     torch.cuda.synchronize()
     O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, w.causal)
     compare(o, lse, O_ref, L_ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_cache_decode(causal):
+    # a few query rows over a million keys (ragged), 256 key splits: the rows against the oracle in full
+    B, H, Lq, Lk, D = 1, 1, 4, 1_000_003, 128
+    inp = ai.make_custom(B, H, Lq, Lk, D, "bf16", causal, seed=170_001)
+    splits = fa.suggest_num_splits(B, H, Lq, Lk, D, causal)
+    note(f"decode over {Lk} keys, causal={causal}, {splits} splits")
+    assert splits == 256
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=inp["scale"], num_splits=splits)
+    o1, l1 = fa.fa_fwd(q, k, v, causal=causal, scale=inp["scale"])
+    torch.cuda.synchronize()
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], causal)
+    compare(o, lse, O_ref, L_ref, "bf16", "long decode split")
+    compare(o1, l1, O_ref, L_ref, "bf16", "long decode one pass")

@@ -240,7 +240,7 @@ def suggest_num_splits(B: int, H: int, Lq: int, Lk: int, D: int, causal: bool, n
         return 1
     keys = Lk - Lq / 2 if causal else Lk  # causal: visible keys of the average row (Lq <= Lk)
     tiles = int(-(-keys // 64))
-    return int(max(1, min(64, num_cu // wgs, tiles // 8)))
+    return int(max(1, min(256, num_cu // wgs, tiles // 8)))
 
 
 def fa_fwd_qkvpacked(qkv: torch.Tensor, o: torch.Tensor | None = None, lse: torch.Tensor | None = None, *,

@@ -22,7 +22,7 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = 256;
 
 int launch_status() {
   const hipError_t e = hipGetLastError();
@@ -363,7 +363,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_DEVICE: return "fa_fwd: no gfx950 kernel for the current device";
     case FA_ERR_LAUNCH: return "fa_fwd: kernel launch failed (see fa_last_hip_error)";
     case FA_ERR_STRIDE: return "fa_fwd: strides must be >= 0, with a row stride of at least D";
-    case FA_ERR_SPLITS: return "fa_fwd_splitkv: num_splits must be between 1 and 64";
+    case FA_ERR_SPLITS: return "fa_fwd_splitkv: num_splits must be between 1 and 256";
     case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1) with round((1 - p) * 256) >= 1";
     case FA_ERR_WORKSPACE: return "workspace smaller than the size query returns (fa_fwd_splitkv / fa_bwd)";
     default: return "fa_fwd: unknown status code";
