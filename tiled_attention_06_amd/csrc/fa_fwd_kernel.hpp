@@ -421,6 +421,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int t_b = __builtin_amdgcn_readfirstlane((int)((int64_t)split * n_kv / p.n_split));
   const int t_e = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * n_kv / p.n_split));
   auto active = [&](int t) { return !CAUSAL || t * BC <= i0w + 31 + off; };  // wave-uniform
+  // a wave whose 32 rows all lie past the last query row only copies and joins
+  const bool live = i0w < p.Lq;  // wave-uniform
 
   // ---- Q tile -> VGPRs, as the B operand of Sᵀ = K·Qᵀ (column = query row l%32,
   // contraction slots of half g = head dims 16s+8g .. 16s+8g+7).  Rows past Lq read 0.
@@ -638,23 +640,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- full tiles, software-pipelined: iteration t computes Sᵀ of tile t+1
     // and its row max while the weights and PV of tile t run; the rescale for
     // tile t uses the max found one iteration earlier.  No mask and no branch
-    // inside the body.
-    compute_s(kst(I0{}), sA);
-    mxA = row_max(sA);
+    // inside the body (a wave with no live rows skips it whole).
+    if (live) {
+      compute_s(kst(I0{}), sA);
+      mxA = row_max(sA);
+    }
     auto it_main = [&](int t, f32x16(&Sc)[KB], f32x16(&Sn)[KB], float& mxc, float& mxn, auto Pc) {
       constexpr int P = decltype(Pc)::value;
       using PN = std::integral_constant<int, (P + 1) % G::NS>;
       using PC = std::integral_constant<int, (P + G::NS - 1) % G::NS>;
-      rescale(mxc);
+      if (live) rescale(mxc);
       if (t + G::NS - 1 < t_e) {
         copy_k(t + G::NS - 1, PC{});
         copy_v(t + G::NS - 1, PC{});
       }
-      compute_s(kst(PN{}), Sn);
-      u32x4 pb[KB][2];
-      make_p(Sc, pb, t);
-      pv(pb, vst(Pc));
-      mxn = row_max(Sn);
+      if (live) {
+        compute_s(kst(PN{}), Sn);
+        u32x4 pb[KB][2];
+        make_p(Sc, pb, t);
+        pv(pb, vst(Pc));
+        mxn = row_max(Sn);
+      }
       end_iter(t);
     };
     static_assert(G::NS == 4, "the loop below is unrolled over the stages");
@@ -667,11 +673,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // weights and PV of the last full tile, whose Sᵀ is already computed
     const int tf = n_full - 1;
     auto finish = [&](f32x16(&Sc)[KB], float mxc) {
-      rescale(mxc);
+      if (live) rescale(mxc);
       if (tf + G::NS - 1 < t_e) copies_rt(tf);
-      u32x4 pb[KB][2];
-      make_p(Sc, pb, tf);
-      pv(pb, vst_rt((tf - t_b) % G::NS));
+      if (live) {
+        u32x4 pb[KB][2];
+        make_p(Sc, pb, tf);
+        pv(pb, vst_rt((tf - t_b) % G::NS));
+      }
       end_iter(tf);
     };
     if ((tf - t_b) & 1)
@@ -684,7 +692,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // masked; a wave skips tiles above its own rows but still copies and joins.
   for (int t = t_tail; t < t_e; ++t) {
     if (t + G::NS - 1 < t_e) copies_rt(t);
-    if (active(t)) {
+    if (live && active(t)) {
       compute_s(kst_rt((t - t_b) % G::NS), sA);
       // (scheduling barriers: the operand reads of one product are not hoisted
       // over the softmax, which would run this path out of registers)
