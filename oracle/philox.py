@@ -28,11 +28,11 @@ iff its byte < T, with T = round((1 − p)·256) in [1, 256]; kept weights are
 scaled by 256 / T, so the expected output equals the output without dropout.
 
 Pins (tests/test_oracle_dropout.py): the Weyl constants against their closed
-forms, byte uniformity and independence statistics, the keep fraction, and
-unbiasedness of the dropped-out attention over many seeds.  The outputs are not
-pinned against published Philox test vectors (the pages print none): parity
-unpinned for bit-identity with other Philox4x32-10 implementations; the GPU
-kernels must reproduce these bits exactly.
+forms, byte uniformity and independence statistics, the keep fraction,
+unbiasedness of the dropped-out attention over many seeds, and the generator's
+output words bit for bit against rocRAND's Philox4x32-10 engine (an independent
+implementation, its header built for the host) on random and extreme counters
+and keys.  The mask layout above is a reading of the pages' silence, not a pin.
 """
 
 from __future__ import annotations

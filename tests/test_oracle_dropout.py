@@ -11,14 +11,18 @@ constants of the key schedule against their closed forms, the statistics of the
 bytes and of the keep-mask, p = 0 giving attention without dropout exactly, LSE
 unaffected, the dropped-out output equal to its definition through the
 (separately pinned) forward oracle's LSE, and unbiasedness over seeds.  The
-generator's outputs are not pinned against published test vectors (none on the
-pages): bit-identity with other Philox4x32-10 implementations is parity unpinned.
+generator itself is pinned bit for bit against an independent implementation,
+rocRAND's Philox4x32-10 engine (host side of its header, built with g++ by the
+test from tests/philox_rocrand_check.cpp), on random and extreme counters and
+keys; planted mistakes in the generator fail that check.
 """
 
 from __future__ import annotations
 
 import math
 import os
+import shutil
+import subprocess
 import sys
 import types
 
@@ -30,6 +34,9 @@ from oracle import philox
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ATTN_SRC = os.path.join(os.path.dirname(HERE), "oracle", "attention.py")
+PHILOX_SRC = os.path.join(os.path.dirname(HERE), "oracle", "philox.py")
+ROCRAND_CHECK = os.path.join(HERE, "philox_rocrand_check.cpp")
+ROCM_INC = "/opt/rocm/include"
 
 
 def test_weyl_constants_closed_forms():
@@ -208,3 +215,88 @@ def test_planted_mistake_is_caught(name):
         except Exception as e:
             failures.append((pin.__name__, type(e).__name__))
     assert failures, f"no pin catches the planted mistake {name!r}"
+
+
+# ---- the generator against rocRAND's Philox4x32-10 ------------------------------------------------
+
+@pytest.fixture(scope="module")
+def rocrand_philox(tmp_path_factory):
+    """Callable (c0, c1, c2, c3, k0, k1 uint32 arrays) -> [n, 4] uint32 from rocRAND's engine."""
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.isfile(os.path.join(ROCM_INC, "rocrand", "rocrand_philox4x32_10.h")):
+        pytest.skip("g++ or rocRAND headers not available")
+    exe = str(tmp_path_factory.mktemp("philox") / "philox_rocrand_check")
+    subprocess.run([gxx, "-O1", "-D__HIP_PLATFORM_AMD__", "-I", ROCM_INC, ROCRAND_CHECK, "-o", exe],
+                   check=True, capture_output=True, timeout=120)
+
+    def run(c0, c1, c2, c3, k0, k1):
+        cols = np.stack([np.asarray(x, dtype=np.uint64) for x in (c0, c1, c2, c3, k0, k1)], axis=1)
+        text = "\n".join(" ".join(str(int(v)) for v in row) for row in cols) + "\n"
+        out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True, timeout=120)
+        return np.array([[int(w) for w in line.split()] for line in out.stdout.splitlines()], dtype=np.uint64)
+
+    return run
+
+
+def _kat_inputs(n=3000, seed=5):
+    rng = np.random.default_rng(seed)
+    full = lambda: rng.integers(0, 2 ** 32, size=n, dtype=np.uint64)
+    c0, c2, c3, k0, k1 = full(), full(), full(), full(), full()
+    c1 = rng.integers(0, 2 ** 30, size=n, dtype=np.uint64)
+    # extremes and the mask's own counters (small block indices, head index, zero word)
+    ext = [(0, 0, 0, 0, 0, 0), (2 ** 32 - 1, 2 ** 30 - 1, 2 ** 32 - 1, 2 ** 32 - 1, 2 ** 32 - 1, 2 ** 32 - 1),
+           (1, 0, 0, 0, 0, 0), (0, 1, 0, 0, 0, 0), (0, 0, 1, 0, 0, 0), (0, 0, 0, 1, 0, 0),
+           (0, 0, 0, 0, 1, 0), (0, 0, 0, 0, 0, 1), (5, 1023, 127, 0, 2024, 0), (1023, 4095, 1, 0, 2024, 7)]
+    ext = np.array(ext, dtype=np.uint64).T
+    return [np.concatenate([a, e]) for a, e in zip((c0, c1, c2, c3, k0, k1), ext)]
+
+
+def _oracle_blocks(mod, c0, c1, c2, c3, k0, k1):
+    outs = [mod.philox4x32_10(c0[i], c1[i], c2[i], c3[i], int(k0[i]), int(k1[i])) for i in range(len(c0))]
+    return np.array([[int(w) for w in o] for o in outs], dtype=np.uint64)
+
+
+def test_philox_matches_rocrand(rocrand_philox):
+    ins = _kat_inputs()
+    ref = rocrand_philox(*ins)
+    # the oracle takes one key per call: group by key is unnecessary, one call per block
+    got = _oracle_blocks(philox, *ins)
+    assert ref.shape == got.shape == (len(ins[0]), 4)
+    bad = np.nonzero(np.any(ref != got, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} blocks differ, first at input {[int(x[bad[0]]) for x in ins]}"
+
+
+def test_philox_vectorised_counters_match_rocrand(rocrand_philox):
+    """The broadcast path the keep-mask uses: many counters under one key in one call."""
+    rng = np.random.default_rng(9)
+    n = 2000
+    c0 = rng.integers(0, 2 ** 32, size=n, dtype=np.uint64)
+    c1 = rng.integers(0, 2 ** 30, size=n, dtype=np.uint64)
+    c2 = rng.integers(0, 2 ** 32, size=n, dtype=np.uint64)
+    k0, k1 = 0x9E3779B9 ^ 12345, 0xDEADBEEF
+    ref = rocrand_philox(c0, c1, c2, np.zeros(n, np.uint64), np.full(n, k0, np.uint64), np.full(n, k1, np.uint64))
+    got = np.stack([np.asarray(w, dtype=np.uint64) for w in philox.philox4x32_10(c0, c1, c2, 0, k0, k1)], axis=1)
+    assert np.array_equal(ref, got)
+
+
+PHILOX_MUTANTS = {
+    "multipliers_swapped": ("p0 = M0 * x0", "p0 = M1 * x0"),
+    "no_key_schedule": ("ka, kb = (ka + W0) & 0xFFFFFFFF, (kb + W1) & 0xFFFFFFFF", "pass"),
+    "nine_rounds": ("for r in range(10):", "for r in range(9):"),
+    "hi_lo_swapped": ("x0, x1, x2, x3 = hi1 ^ x1 ^ np.uint64(ka), lo1,", "x0, x1, x2, x3 = lo1 ^ x1 ^ np.uint64(ka), hi1,"),
+    "key_words_swapped": ("hi1 ^ x1 ^ np.uint64(ka), lo1, hi0 ^ x3 ^ np.uint64(kb)",
+                          "hi1 ^ x1 ^ np.uint64(kb), lo1, hi0 ^ x3 ^ np.uint64(ka)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PHILOX_MUTANTS))
+def test_planted_generator_mistake_is_caught(name, rocrand_philox):
+    old, new = PHILOX_MUTANTS[name]
+    with open(PHILOX_SRC, encoding="utf-8") as f:
+        src = f.read()
+    assert old in src, f"mutation anchor for {name} not found"
+    mod = types.ModuleType(f"oracle.philox_mutant_{name}")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new, 1), PHILOX_SRC + f"<{name}>", "exec"), mod.__dict__)
+    ins = [x[:200] for x in _kat_inputs(n=200)]
+    assert not np.array_equal(rocrand_philox(*ins), _oracle_blocks(mod, *ins))
