@@ -4,6 +4,7 @@
     python bench.py --traffic-probe          # for rocprofv3 --pmc runs (see below)
     python bench.py --summarize-traffic DIR  # FETCH_SIZE/WRITE_SIZE CSVs -> profiles/*_traffic.md
     python bench.py --summarize-trace DIR    # kernel-trace stats CSV -> profiles/*_kernel_trace.md
+    python bench.py --summarize-counters DIR # SQ counter CSVs -> profiles/*_sq_counters.md
     python bench.py --pass bwd [--workload W] # the backward pass (fa_bwd) instead of the forward
 
 One step = one ``fa_fwd`` call (the whole hot path: one kernel) over the
@@ -303,6 +304,91 @@ def summarize_traffic(directory: str, w, pass_: str = "fwd") -> str:
     return "\n".join(lines)
 
 
+# Shader-sequencer counters of the forward kernel, three rocprofv3 --pmc runs of
+# `bench.py --traffic-probe` (at most 8 SQ counters per run).
+SQ_PASSES = (
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE",
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+    "SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_MISC SQ_ACTIVE_INST_VALU2 GRBM_GUI_ACTIVE",
+    "SQ_THREAD_CYCLES_VALU SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL "
+    "SQ_LDS_ADDR_CONFLICT SQ_ACTIVE_INST_SCA SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+)
+N_CU, N_SIMD, N_XCC = 256, 1024, 8
+
+
+def summarize_counters(directory: str, w) -> str:
+    """Mean per fa_fwd_kernel dispatch of the SQ counters, and what they say about the SIMDs' time."""
+    rows = _csv_rows(directory, "*counter_collection.csv")
+    per = {}
+    dur = {}
+    for r in rows:
+        if "fa_fwd_kernel" not in r["Kernel_Name"]:
+            continue
+        key = (r["Agent_Id"], r["Dispatch_Id"], r["Process_Id"])
+        per.setdefault(r["Counter_Name"], {})[key] = float(r["Counter_Value"])
+        dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    need = [c for p_ in SQ_PASSES for c in p_.split()]
+    missing = [c for c in need if c not in per]
+    if missing:
+        raise SystemExit(f"counters missing for fa_fwd_kernel: {missing}")
+    m = {c: sum(v.values()) / len(v) for c, v in per.items()}
+    secs = sum(dur.values()) / len(dur)
+    cyc = m["GRBM_GUI_ACTIVE"] / N_XCC              # GPU cycles per dispatch (summed over the XCDs)
+    waves = 2 * N_SIMD                              # wave slots in use: two waves per SIMD
+    q = 4.0                                         # "quad-cycle" counters count units of 4 cycles
+    mfma = m["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cyc
+    valu = m["SQ_ACTIVE_INST_VALU"] * q / N_SIMD / cyc
+    coex = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / N_SIMD / cyc
+    resident = m["SQ_WAVE_CYCLES"] * q / waves / cyc
+    act = m["SQ_ACTIVE_INST_ANY"] * q / waves / cyc
+    wait = m["SQ_WAIT_ANY"] * q / waves / cyc
+    wait_issue = m["SQ_WAIT_INST_ANY"] * q / waves / cyc
+    lds = m["SQ_LDS_IDX_ACTIVE"] / N_CU / cyc
+    n_mfma = m["SQ_INSTS_MFMA"]
+    mfma_flop = n_mfma * 2 * 32 * 32 * 16
+    lines = [
+        f"# SQ counters: fa_fwd_kernel on {w.name} ({w.description})",
+        "",
+        "Three `rocprofv3 --pmc` runs of `bench.py --traffic-probe` (a copy, then 3 calls of fa_fwd), one per",
+        "counter set; the values below are means over the fa_fwd_kernel dispatches.  Commands (from the",
+        "repository root on the GPU box; rocprofv3 collects at most 8 SQ counters per run):",
+        "",
+    ]
+    for i, p_ in enumerate(SQ_PASSES):
+        lines.append(f"    rocprofv3 --pmc {p_} --output-format csv -d gpurun_out/sq{i} -o sq -- python3 bench.py "
+                     "--traffic-probe")
+    lines += [
+        "    python3 bench.py --summarize-counters gpurun_out  (reads the three directories)",
+        "",
+        "Raw means per dispatch:",
+        "",
+        *[f"    {c:28s} {m[c]:.6g}" for c in sorted(set(need))],
+        "",
+        f"Derived (MI355X: {N_CU} CUs, {N_SIMD} SIMDs, {N_XCC} XCDs; GRBM_GUI_ACTIVE counts per XCD; the kernel runs",
+        "two waves per SIMD; SQ_ACTIVE_*, SQ_WAIT_* and SQ_WAVE_CYCLES count quad-cycles per wave):",
+        "",
+        f"    dispatch duration                          {secs * 1e6:.1f} us (counter runs, 3 cold calls)",
+        f"    GPU cycles per dispatch                    {cyc:.4g}  -> shader clock {cyc / secs / 1e9:.2f} GHz",
+        f"    MFMA instructions per dispatch             {n_mfma:.5g} (v_mfma_f32_32x32x16: {mfma_flop:.4g} flop;"
+        f" metric FLOP {w.flops:.4g}, ratio {mfma_flop / w.flops:.3f})",
+        f"    MFMA busy, fraction of SIMD cycles         {mfma:.3f}",
+        f"    VALU issue (both waves), fraction          {valu:.3f}",
+        f"    MFMA busy while VALU issues (co-execution) {coex:.3f}",
+        f"    neither (1 - MFMA - VALU + co-execution)   {max(0.0, 1 - mfma - valu + coex):.3f}",
+        f"    non-MFMA VALU instructions per MFMA        {(m['SQ_INSTS_VALU'] - n_mfma) / n_mfma:.2f}",
+        f"    LDS instructions per MFMA                  {m['SQ_INSTS_LDS'] / n_mfma:.2f}",
+        f"    LDS busy (indexed ops), fraction of CU     {lds:.3f}; bank conflicts {m['SQ_LDS_BANK_CONFLICT']:.0f}",
+        f"    wave slots occupied                        {resident:.3f}",
+        f"    per resident wave: issuing {act / resident:.3f}, waiting (waitcnt/barrier) {wait / resident:.3f}, "
+        f"ready but not issued {wait_issue / resident:.3f}",
+        "",
+        f"kernel_source_sha256: {kernel_source_hash('fwd')}",
+        "",
+    ]
+    return "\n".join(lines)
+
+
 def summarize_trace(directory: str, w, bench_line: str | None, pass_: str = "fwd") -> str:
     rows = _csv_rows(directory, "*kernel_stats.csv")
     if not rows:
@@ -432,6 +518,7 @@ def main() -> int:
     ap.add_argument("--traffic-probe", action="store_true")
     ap.add_argument("--summarize-traffic", metavar="DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-counters", metavar="DIR", help="SQ counter CSVs -> profiles/*_sq_counters.md")
     ap.add_argument("--bench-log", metavar="FILE", help="bench JSON line to quote in the trace summary")
     args = ap.parse_args()
 
@@ -447,6 +534,13 @@ def main() -> int:
     if args.summarize_traffic:
         text = summarize_traffic(args.summarize_traffic, w, args.pass_)
         with open(TRAFFIC_FILES[args.pass_], "w", encoding="utf-8") as f:
+            f.write(text)
+        print(text)
+        return 0
+    if args.summarize_counters:
+        text = summarize_counters(args.summarize_counters, w)
+        with open(os.path.join(ROOT, "profiles", f"fa_fwd_kernel_{w.name}_sq_counters.md"), "w",
+                  encoding="utf-8") as f:
             f.write(text)
         print(text)
         return 0
