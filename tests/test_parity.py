@@ -90,6 +90,26 @@ def test_edge_shapes(B, H, Lq, Lk, D, dtype, causal):
     compare(o, lse, O_ref, L_ref, dtype, "edge")
 
 
+# Grids of 256-row workgroups larger than the CU count (256 on MI355X) run 8 waves per
+# workgroup; smaller ones (every case above) run 4 waves and 128 rows.  These cases keep
+# ragged tails and both sides of that boundary covered for the 8-wave form.
+WIDE = [(1, 300, 300, 300, 64, "fp16", True), (1, 300, 300, 300, 128, "bf16", False),
+        (2, 130, 129, 1000, 128, "bf16", False), (1, 257, 65, 65, 64, "bf16", True),
+        (1, 256, 65, 65, 128, "fp16", True), (1, 257, 65, 65, 128, "fp16", True),
+        (4, 40, 700, 700, 128, "bf16", True)]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal", WIDE,
+                         ids=[f"B{b}H{h}_{lq}x{lk}_D{d}_{dt}_{'c' if c else 'nc'}" for b, h, lq, lk, d, dt, c in WIDE])
+def test_wide_grids(B, H, Lq, Lk, D, dtype, causal):
+    seed = 20_000 + 7 * H + 97 * Lq + 13 * Lk + D + (1 if causal else 0)
+    inp = ai.make_custom(B, H, Lq, Lk, D, dtype, causal, seed=seed)
+    note(f"wide B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype} causal={causal} seed={seed}")
+    o, lse = run_gpu(inp)
+    O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], causal)
+    compare(o, lse, O_ref, L_ref, dtype, "wide")
+
+
 # ------------------------------------------------------------------------------------------
 # the five workloads at full size, in the launch configuration the bench times
 # ------------------------------------------------------------------------------------------

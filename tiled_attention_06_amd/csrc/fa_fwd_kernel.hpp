@@ -6,7 +6,9 @@
 //   [OP] "FlashAttention优化原理与工程实践"                (lbrq.cn/news/50349)
 //
 // One workgroup = 8 waves (two per SIMD) = 256 query rows of one (batch, head);
-// each wave owns 32 rows.  One workgroup per CU.  The method ([DF §2.2], first
+// each wave owns 32 rows.  One workgroup per CU.  (Grids with no more such
+// workgroups than CUs use 4 waves and 128 rows instead: twice the workgroups,
+// one wave per SIMD.)  The method ([DF §2.2], first
 // and second layers; [OP §2.1], a loop over key blocks inside a loop over query
 // blocks):
 //   * the Q tile is loaded once and stays in VGPRs as MFMA operands;
@@ -276,10 +278,12 @@ __device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Tile geometry shared by the kernel and the host launcher.
-template <int D>
+// Tile geometry shared by the kernel and the host launcher.  NW_ = 8: two waves
+// per SIMD, 256 query rows per workgroup (the default); NW_ = 4: one wave per
+// SIMD and 128 rows, for grids too small to give every CU a workgroup otherwise.
+template <int D, int NW_ = 8>
 struct Geo {
-  static constexpr int NW = 8;                 // waves per workgroup (two per SIMD)
+  static constexpr int NW = NW_;               // waves per workgroup
   static constexpr int NT = 64 * NW;           // threads per workgroup
   static constexpr int BR = 32 * NW;           // query rows per workgroup
   static constexpr int BC = 64;                // keys per K/V tile
@@ -303,9 +307,9 @@ struct Geo {
   static_assert(LDS <= 163840, "one workgroup per CU");
 };
 
-template <int D, int DT, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(FwdParams p) {
-  using G = Geo<D>;
+template <int D, int DT, bool CAUSAL, bool DROP, int NW = 8>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(FwdParams p) {
+  using G = Geo<D, NW>;
   constexpr int BC = G::BC, KB = G::KB, NB = G::NB, KS = G::KS, NCH = G::NCH;
   constexpr int NBLK = G::NBLK, KBS = G::KBS, VBS = G::VBS, KT = G::KT, VT = G::VT;
   constexpr float NEG_INF = -__builtin_inff();
