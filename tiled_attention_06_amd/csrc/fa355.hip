@@ -122,8 +122,8 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   for (int i = 0; i < 4; ++i)
     if (((lens[i] + 256) * st[i][2] + D) * 2 >= (1ll << 32)) return FA_ERR_SHAPE;
   if (splits > 1 && ((int64_t)Lq + 256) * D * 4 >= (1ll << 32)) return FA_ERR_SHAPE;  // one partial slab
-  // Workgroups of 8 waves and 256 rows; a single pass (no key splits, no dropout)
-  // whose grid would not exceed the CU count takes 4 waves and 128 rows instead:
+  // Workgroups of 8 waves and 256 rows; a single pass (no key splits) whose grid
+  // would not exceed the CU count takes 4 waves and 128 rows instead:
   // twice the workgroups, and the heaviest causal ones half as long (measured on
   // the 1x32x2048x128 causal shape: 59.4 -> 51.6 us; on larger grids the
   // 8-wave form is faster).
@@ -132,7 +132,7 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                 "row tile independent of D");
   int64_t n_qt = ((int64_t)Lq + BR8 - 1) / BR8;
   bool narrow = false;
-  if (splits == 1 && drop_t == 256 && (int64_t)B * H * n_qt <= 2048) {
+  if (splits == 1 && (int64_t)B * H * n_qt <= 2048) {
     const int cus = cu_count();
     narrow = cus > 0 && (int64_t)B * H * n_qt <= cus;
   }
@@ -184,9 +184,13 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   m.o_sb = p.o_sb, m.o_sh = p.o_sh, m.o_sl = p.o_sl;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (drop_t < 256)  // (only the single-pass entry point takes a dropout probability)
+  if (drop_t < 256) {  // (only the single-pass entry point takes a dropout probability)
+    if (narrow)
+      return D == 128 ? dispatch_dtype<128, true, 4>(p, m, dtype, causal != 0, s)
+                      : dispatch_dtype<64, true, 4>(p, m, dtype, causal != 0, s);
     return D == 128 ? dispatch_dtype<128, true>(p, m, dtype, causal != 0, s)
                     : dispatch_dtype<64, true>(p, m, dtype, causal != 0, s);
+  }
   if (narrow)
     return D == 128 ? dispatch_dtype<128, false, 4>(p, m, dtype, causal != 0, s)
                     : dispatch_dtype<64, false, 4>(p, m, dtype, causal != 0, s);
