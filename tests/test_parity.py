@@ -110,6 +110,20 @@ def test_wide_grids(B, H, Lq, Lk, D, dtype, causal):
     compare(o, lse, O_ref, L_ref, dtype, "wide")
 
 
+@pytest.mark.parametrize("D,dtype,causal", [(128, "bf16", True), (64, "fp16", False), (128, "fp16", False)])
+def test_geometry_bitwise(D, dtype, causal):
+    # 300 heads of 520 rows (3 query tiles of 256: 900 workgroups, the 8-wave form) against the
+    # first 4 heads alone (12 workgroups, the 4-wave form): every row is computed the same way in
+    # either grouping, so the two must agree bit for bit
+    inp = ai.make_custom(1, 300, 520, 520, D, dtype, causal, seed=31_000 + D)
+    note(f"geometry B1 H300 L520 D{D} {dtype} causal={causal}")
+    o_all, l_all = run_gpu(inp)
+    few = {n: inp[n][:, :4].contiguous() for n in ("q", "k", "v")}
+    o_few, l_few = run_gpu({**inp, **few})
+    assert torch.equal(o_all[:, :4], o_few), "O differs between the 8-wave and 4-wave forms"
+    assert torch.equal(l_all[:, :4], l_few), "LSE differs between the 8-wave and 4-wave forms"
+
+
 # ------------------------------------------------------------------------------------------
 # the five workloads at full size, in the launch configuration the bench times
 # ------------------------------------------------------------------------------------------
