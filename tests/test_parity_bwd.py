@@ -163,6 +163,23 @@ def test_bwd_workload_sampled(name):
     compare(got, ref, w.dtype, f"bwd {name}", heads=heads, extra=extra)
 
 
+@pytest.mark.parametrize("D,dtype,causal", [(64, "fp16", True), (128, "bf16", False)])
+def test_bwd_wide_grid_and_geometry(D, dtype, causal):
+    # 300 heads of 300 rows: 600 dQ workgroups (ragged tails), checked on three heads against the oracle;
+    # the first 4 heads alone (a grid smaller than the CU count) must give bit-identical gradients
+    inp = ai.make_custom(1, 300, 300, 300, D, dtype, causal, seed=95_000 + D)
+    do = ai.make_dout((1, 300, 300, D), dtype, seed=95_100 + D)
+    note(f"bwd wide B1 H300 300x300 D{D} {dtype} causal={causal}")
+    got = run_bwd(inp, do, causal)
+    heads = [(0, 0), (0, 150), (0, 299)]
+    ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, inp["scale"], causal, heads=heads)
+    compare(got, ref, dtype, "bwd wide", heads=heads)
+    few = {n: inp[n][:, :4].contiguous() for n in ("q", "k", "v")}
+    got4 = run_bwd({**inp, **few}, do[:, :4].contiguous(), causal)
+    for name, x, y in zip(("dq", "dk", "dv"), got, got4):
+        assert torch.equal(x[:, :4], y), f"{name} of the first 4 heads depends on the grid"
+
+
 def test_bwd_deterministic():
     inp = ai.make_custom(1, 4, 700, 700, 128, "bf16", True, seed=90_001)
     do = ai.make_dout((1, 4, 700, 128), "bf16", seed=90_002)
