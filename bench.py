@@ -26,7 +26,10 @@ Besides the contract fields the line carries:
     launch duration, measured with HIP events recorded on the launch stream
     around every timed launch; ``traffic`` is the HBM bytes per launch from the
     committed rocprofv3 counter summary, reported only while the kernel sources
-    still hash to what was profiled (else null);
+    still hash to what was profiled (else null), and ``traffic_gbs`` that over
+    this run's mean launch time; ``counters``: the fractions of SIMD cycles with
+    the matrix cores busy, with VALU issue, with both, and of CU cycles with LDS
+    busy, from the committed SQ counter summary under the same hash rule;
   * ``cpu_baseline``: the fp64 CPU oracle timed on this host over a bounded
     sample of the same workload (whole heads, every row), as TFLOP/s-equivalent;
   * ``parity``: a sampled comparison of this run's output with the oracle.
@@ -90,6 +93,30 @@ def committed_traffic(workload: str, pass_: str = "fwd"):
     if not m or not b or m.group(1) != kernel_source_hash(pass_):
         return None
     return float(b.group(1))
+
+
+def committed_sq_counters(workload: str):
+    """Fractions of SIMD cycles from the committed SQ counter summary, if it matches the current kernels."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_kernel_{workload}_sq_counters.md")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or m.group(1) != kernel_source_hash("fwd"):
+        return None
+    keys = {"mfma_busy": r"MFMA busy, fraction of SIMD cycles\s+([0-9.]+)",
+            "valu_issue": r"VALU issue \(both waves\), fraction\s+([0-9.]+)",
+            "mfma_valu_overlap": r"MFMA busy while VALU issues \(co-execution\)\s+([0-9.]+)",
+            "lds_busy": r"LDS busy \(indexed ops\), fraction of CU\s+([0-9.]+)"}
+    out = {}
+    for k, rx in keys.items():
+        r = re.search(rx, text)
+        if not r:
+            return None
+        out[k] = float(r.group(1))
+    out["source"] = os.path.relpath(path, ROOT)
+    return out
 
 
 def cpu_baseline(inp, budget_s: float = 10.0, dropout_p: float = 0.0) -> dict:
@@ -623,6 +650,11 @@ def main() -> int:
                 "frac": round(gbs / PEAK_HBM_GBS, 5), "tflops": round(achieved, 3)}
     roof.update({"traffic": traffic, "kernel": kname, "mean_launch_us": round(mean_kernel_s * 1e6, 3),
                  "algorithmic_bytes": w.hbm_bytes})
+    if traffic is not None:  # bytes beyond L2 per launch (counters) over this run's mean launch time
+        roof["traffic_gbs"] = round(traffic / mean_kernel_s / 1e9, 1)
+    sq = committed_sq_counters(w.name) if splits == 1 and not args.dropout else None
+    if sq is not None:  # SIMD-cycle fractions from the committed SQ counter profile of this kernel
+        roof["counters"] = sq
     out = {
         "metric": (METRIC if w.name == "train7b_4k" and not args.dropout
                    else f"attention fwd TFLOP/s ({w.description}{f', dropout {args.dropout}' if args.dropout else ''})"),
