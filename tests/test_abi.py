@@ -152,6 +152,16 @@ def test_strided_row_stride_limit(which):
     assert call_strided(strides={which: (0, 0, 1 << 24)}) == -2
 
 
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_strided_row_stride_overflow(which):
+    # a row stride whose 64-bit size product ((L + 256)·s + D)·2 wraps past 2^64 to a small
+    # number (L = 64 here: 640·(2^57 + 8) + 256 = 5·2^64 + 5376) is still rejected
+    s = (1 << 57) + 8
+    assert s % 8 == 0 and ((64 + 256) * s + 128) * 2 % (1 << 64) < (1 << 32)
+    assert call_strided(strides={which: (0, 0, s)}) == -2
+    assert call_strided(strides={which: (0, 0, (1 << 63) - 8)}) == -2
+
+
 def test_strided_valid_strides_reach_later_checks():
     # broadcast K/V (batch and head stride 0) and padded rows are accepted; a later
     # check (head dim) fails, so nothing launches
@@ -369,4 +379,8 @@ def test_bwd_strided_checks():
     big = list(good)
     big[3 * 1 + 2] = 1 << 22                                          # k rows beyond 32-bit offsets
     assert call_bwd_strided(strides=big) == -2
+    for t in range(8):                                                # a row stride whose size product wraps
+        big = list(good)
+        big[3 * t + 2] = 28_823_037_615_171_176
+        assert call_bwd_strided(strides=big) == -2
     assert call_bwd_strided(p=1.0) == -13

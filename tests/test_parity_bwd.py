@@ -10,9 +10,10 @@ with TOL = 1e-2 (bf16) / 2e-3 (fp16) and TOL_RMS = 6e-3 / 8e-4, plus an absolute
 1e-5 for slabs whose exact gradient is 0 (one visible key: the kernel's dP − Δ is
 then an fp32 rounding residue, ~1e-7 at unit-scale inputs).  Derivation: the
 kernels round P and dS to the input type as matrix-core operands and round the
-outputs; emulating exactly those roundings on the CPU (fp64 otherwise) gives at
-most 4.4e-3 / 5.5e-4 of the slab's max and 2.5e-3 / 3.1e-4 of its rms, at
-L = 300..1024, D = 64 and 128, causal and not.  The bars are 2.3–3.6x those.
+outputs; the CPU model of exactly those roundings in fp32 (numerics.emulate, with
+O and LSE from the modelled forward pass) gives at most 6.2e-3 / 1.2e-3 of the
+slab's max and 2.7e-3 / 3.6e-4 of its rms, at L = 300..1024, D = 64 and 128,
+causal and not (tests/test_numerics.py).  The bars are 1.6–2.3x those.
 Outputs are pre-filled with NaN so that an unwritten element fails.
 """
 
@@ -49,7 +50,7 @@ def run_bwd(inp, do, causal, scale=None):
 
 
 def compare(got, ref, dtype, what, heads=None, extra=None):
-    """extra: optional {(b, h): (dq row bounds, dk row bounds)} added to the bars (see bwd_bounds)."""
+    """extra: optional {(b, h): (dq row bounds, dk row bounds)} added to the bars (numerics.delta_bounds)."""
     names = ("dq", "dk", "dv")
     for t, (name, g, r) in enumerate(zip(names, got, ref)):
         g = g.double().numpy()
@@ -127,10 +128,10 @@ def test_bwd_sum_rules_at_train_shape():
 
 def test_bwd_peaked_softmax():
     # the numerics-stress recipe (Q ~ N(0, 3²) boosted so one key per row leads by 20 logits) at L = 1024:
-    # dQ and dK are then ~1e-7, of the order of what rounding the stored O moves Δ by (bwd_bounds)
+    # dQ and dK are then ~1e-7, of the order of what rounding the stored O moves Δ by (numerics.delta_bounds)
     import dataclasses
 
-    from bwd_bounds import delta_bounds
+    from numerics import delta_bounds
     from oracle import attention_fp64
 
     w = dataclasses.replace(ai.WORKLOADS["stress_8k"], B=1, H=2, Lq=1024, Lk=1024)
@@ -147,7 +148,7 @@ def test_bwd_peaked_softmax():
 @pytest.mark.parametrize("name", ["llama7b_2k", "stress_8k", "long_16k"])
 def test_bwd_workload_sampled(name):
     # the other workloads at full size: every head on the GPU, one or two heads in full against the oracle
-    from bwd_bounds import delta_bounds
+    from numerics import delta_bounds
     from oracle import attention_fp64
 
     w = ai.WORKLOADS[name]

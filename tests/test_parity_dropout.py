@@ -3,8 +3,10 @@
 The keep bits are integer decisions on Philox4x32-10 bytes, taken identically by
 the kernels and by oracle/philox.py: a single differing bit changes an output row
 by O(1), far beyond the bars.  The bars are those of the dropout-free tests: the
-forward's (2e-3 fp16 / 1e-2 bf16 per element, or one output ulp where larger; LSE
-1e-3) and the backward's (per slab, relative to the slab's max and rms).
+forward's (2e-3 fp16 / 1e-2 bf16 per element, or, only where the output format is
+coarser than that, its rounding plus the bound of the kernel's weight rounding,
+numerics.fwd_allowance with the keep mask; LSE 1e-3) and the backward's (per slab,
+relative to the slab's max and rms).
 """
 
 from __future__ import annotations
@@ -44,7 +46,7 @@ def test_dropout_forward(B, H, Lq, Lk, D, dtype, causal, p, seed):
     _, lse0 = fa.fa_fwd(q, k, v, causal=causal, scale=inp["scale"])
     torch.cuda.synchronize()
     O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], causal, dropout_p=p, seed=seed)
-    compare_fwd(o, lse, O_ref, L_ref, dtype, "dropout fwd")
+    compare_fwd(o, lse, O_ref, L_ref, dtype, "dropout fwd", src=dict(inp, dropout_p=p, seed=seed))
     assert torch.equal(lse.cpu(), lse0.cpu()), "LSE must not depend on dropout"
 
 
@@ -115,9 +117,8 @@ def test_dropout_train_shape_sampled():
     heads, rows = _sample(w, seed=11)
     O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], w.scale, True, rows=rows, heads=heads,
                                   dropout_p=p, seed=seed)
-    oc, lc = o.cpu(), lse.cpu()
-    for b, h in heads:
-        compare_fwd(oc[b, h][rows], lc[b, h][rows], O_ref[b, h], L_ref[b, h], w.dtype, f"dropout train ({b},{h})")
+    compare_fwd(o.cpu()[:, :, rows], lse.cpu()[:, :, rows], O_ref, L_ref, w.dtype, "dropout train",
+                src=dict(inp, dropout_p=p, seed=seed), heads=heads, rows=rows)
     bh = [(0, 0), (w.B - 1, w.H - 1)]
     ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, w.scale, True, heads=bh, dropout_p=p, seed=seed)
     compare_bwd((dq.cpu(), dk.cpu(), dv.cpu()), ref, w.dtype, "dropout train bwd", heads=bh)

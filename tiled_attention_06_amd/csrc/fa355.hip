@@ -117,10 +117,12 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   }
 
   // One head's slab is addressed with 32-bit byte offsets, including up to 256
-  // rows of tile padding past its end; batch and head offsets are 64-bit.
+  // rows of tile padding past its end: (len + 256)·row_stride + D elements must
+  // stay below 2^31 (checked by division, so that no product can overflow);
+  // batch and head offsets are 64-bit.
   const int64_t lens[4] = {Lq, Lk, Lk, Lq};
   for (int i = 0; i < 4; ++i)
-    if (((lens[i] + 256) * st[i][2] + D) * 2 >= (1ll << 32)) return FA_ERR_SHAPE;
+    if (st[i][2] > ((1ll << 31) - 1 - D) / (lens[i] + 256)) return FA_ERR_SHAPE;
   if (splits > 1 && ((int64_t)Lq + 256) * D * 4 >= (1ll << 32)) return FA_ERR_SHAPE;  // one partial slab
   // Workgroups of 8 waves and 256 rows; a single pass (no key splits) whose grid
   // would not exceed the CU count takes 4 waves and 128 rows instead:
@@ -267,8 +269,8 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
   if (drop_t < 0) return FA_ERR_DROPOUT;
   if (ws_size < bwd_ws_bytes(B, H, Lq)) return FA_ERR_WORKSPACE;
   // one head's slab plus a tile of padding in 32-bit byte offsets
-  for (int i = 0; i < 8; ++i)
-    if (((len[i] + 256) * st[i][2] + D) * 2 >= (1ll << 32)) return FA_ERR_SHAPE;
+  for (int i = 0; i < 8; ++i)  // (len + 256)·row_stride + D < 2^31, by division (no overflow)
+    if (st[i][2] > ((1ll << 31) - 1 - D) / (len[i] + 256)) return FA_ERR_SHAPE;
   const int64_t n_qt = ((int64_t)Lq + kBwdDqRows - 1) / kBwdDqRows;
   const int64_t n_kt = ((int64_t)Lk + kBwdKvKeys - 1) / kBwdKvKeys;
   if ((int64_t)B * H >= (1ll << 31) || (int64_t)B * H * n_qt >= (1ll << 22) || (int64_t)B * H * n_kt >= (1ll << 22))
