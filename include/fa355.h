@@ -155,6 +155,35 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    size_t workspace_bytes, fa_stream_t stream);
 
 /*
+ * fa_fwd_splitkv_noalloc — fa_fwd_splitkv without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory at the
+ * time of the call: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation.
+ *
+ * The partials live in a device array of FA_NOALLOC_SCRATCH_BYTES compiled into
+ * the library; each GPU the library runs on holds its own copy from the first
+ * call on that GPU until the process ends.  The arguments and results are those
+ * of fa_fwd_splitkv with the same num_splits (the same kernels; bitwise equal
+ * outputs).  The call allocates nothing (no hipMalloc, no library allocation);
+ * its first call on a device looks up that device's copy of the array once.
+ *
+ *   fa_fwd_splitkv_workspace_size(B, H, Lq, D, num_splits) must not exceed
+ *   FA_NOALLOC_SCRATCH_BYTES (FA_ERR_WORKSPACE otherwise; nothing enqueued).
+ *   num_splits = 1 is fa_fwd_strided and touches no scratch memory.
+ *
+ * Every call on one GPU uses that GPU's one array: calls that may overlap on a
+ * GPU (different streams, or different host threads without ordering) race on
+ * it and give wrong results; order them on one stream.  No part of the array
+ * needs clearing between calls (each call writes every partial it reads).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                           int Lk, int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                           const int64_t* o_stride, float scale, int causal, int dtype, int num_splits,
+                           fa_stream_t stream);
+
+/*
  * fa_bwd — enqueue the attention backward pass on `stream`: the gradients of
  * o (the forward operation above) with respect to q, k and v for an upstream
  * gradient dout of o.

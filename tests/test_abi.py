@@ -49,7 +49,7 @@ def call_strided(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, Lq=64, Lk=6
 
 def test_header_declares_the_abi():
     assert declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-                                    "fa_bwd_workspace_size", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout",
+                                    "fa_fwd_splitkv_noalloc", "fa_bwd_workspace_size", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout",
                                     "fa_fwd_dropout_strided", "fa_bwd_strided", "fa_status_string",
                                     "fa_last_hip_error", "fa_version"]
 
@@ -231,6 +231,42 @@ def call_split(splits=2, ws=P[4] * 16, ws_bytes=None, B=1, H=2, Lq=300, Lk=500, 
     args.update(kw)
     return fa.lib.fa_fwd_splitkv(args["q"], args["k"], args["v"], args["o"], args["lse"], B, H, Lq, Lk, D, *ptr,
                                  args["scale"], args["causal"], args["dtype"], splits, ws, ws_bytes, None)
+
+
+def call_noalloc(splits=2, B=1, H=2, Lq=300, Lk=500, D=128, **kw):
+    st = {"q": (H * Lq * D, Lq * D, D), "k": (H * Lk * D, Lk * D, D), "v": (H * Lk * D, Lk * D, D),
+          "o": (H * Lq * D, Lq * D, D)}
+    st.update(kw.pop("strides", {}))
+    arr = [None if st[n] is None else (ctypes.c_int64 * 3)(*st[n]) for n in ("q", "k", "v", "o")]
+    ptr = [None if a is None else ctypes.cast(a, ctypes.c_void_p) for a in arr]
+    args = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], scale=0.125, causal=0, dtype=1)
+    args.update(kw)
+    return fa.lib.fa_fwd_splitkv_noalloc(args["q"], args["k"], args["v"], args["o"], args["lse"], B, H, Lq, Lk, D,
+                                         *ptr, args["scale"], args["causal"], args["dtype"], splits, None)
+
+
+def test_noalloc_argument_checks():
+    # every argument fault is reported before the call touches HIP (no GPU here)
+    for which in ("q", "k", "v", "o", "lse"):
+        assert call_noalloc(**{which: None}) == -1
+    assert call_noalloc(strides={"k": None}) == -1
+    assert call_noalloc(splits=0) == -11 and call_noalloc(splits=257) == -11
+    assert call_noalloc(D=96) == -3 and call_noalloc(dtype=2) == -4
+    assert call_noalloc(scale=float("nan")) == -6
+    assert call_noalloc(causal=1, Lq=501, Lk=500) == -7
+    assert call_noalloc(strides={"o": (0, 0, 28_823_037_615_171_176)}) == -2
+    # partials beyond the scratch array: FA_ERR_WORKSPACE, nothing enqueued
+    cap = fa.FA_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_fwd_splitkv_workspace_size(1, 32, 256, 128, 16) > cap      # 16 splits of 32 x 256 rows
+    assert call_noalloc(splits=16, B=1, H=32, Lq=256, Lk=16384) == -12
+    assert fa.fa_fwd_splitkv_workspace_size(1, 32, 256, 128, 8) <= cap      # 8 of them fit
+    assert call_noalloc(splits=8, B=1, H=32, Lq=256, Lk=16384, scale=float("inf")) == -6
+
+
+def test_noalloc_scratch_size_in_header():
+    with open(HEADER, encoding="utf-8") as f:
+        m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)", f.read())
+    assert m and int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == fa.FA_NOALLOC_SCRATCH_BYTES
 
 
 def test_splitkv_workspace_size():

@@ -9,7 +9,7 @@ Names follow the C ABI: ``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_status_string``, ``fa_last_hip_error``,
 ``fa_version``, ``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_fwd_dropout``,
 ``fa_bwd_dropout``, ``fa_fwd_dropout_strided``, ``fa_bwd_strided`` (reached through ``fa_fwd`` /
-``fa_bwd`` with views and ``dropout_p``); ``fa_fwd_qkvpacked`` is a
+``fa_bwd`` with views and ``dropout_p``), ``fa_fwd_splitkv_noalloc``; ``fa_fwd_qkvpacked`` is a
 view helper over ``fa_fwd_strided`` for a packed [B, L, 3, H, D] qkv buffer,
 ``suggest_num_splits`` a host heuristic, and ``flash_attention`` an autograd
 function whose forward is ``fa_fwd`` and whose backward is ``fa_bwd``.
@@ -24,6 +24,7 @@ import os
 import torch
 
 __all__ = ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_qkvpacked",
+           "fa_fwd_splitkv_noalloc", "FA_NOALLOC_SCRATCH_BYTES",
            "suggest_num_splits", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout",
            "flash_attention", "fa_status_string",
            "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH", "FA_DTYPE_F16", "FA_DTYPE_BF16"]
@@ -49,6 +50,9 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, ctypes.c_float, i, i, i, vp,
                                    ctypes.c_size_t, vp]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, ctypes.c_float, i, i,
+                                           i, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = i
     lib.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp] * 9 + [i] * 5 + [ctypes.c_float, i, i, vp, ctypes.c_size_t, vp]
@@ -224,6 +228,33 @@ def fa_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
     if num_splits == 1:
         return _launch(True, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream)
     return _launch(True, q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream, num_splits, workspace)
+
+
+FA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # the scratch array of fa_fwd_splitkv_noalloc (include/fa355.h)
+
+
+def fa_fwd_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                           *, causal: bool = False, scale: float | None = None, num_splits: int = 2,
+                           stream: torch.cuda.Stream | None = None):
+    """The C ``fa_fwd_splitkv_noalloc``: ``fa_fwd_splitkv`` with its partials in the library's own device
+    array (at most FA_NOALLOC_SCRATCH_BYTES), so that neither this call nor the library allocates.  o and
+    lse must be given (this wrapper allocates nothing either).  Calls that may overlap on one GPU race on
+    the shared array."""
+    if o is None or lse is None:
+        raise ValueError("fa_fwd_splitkv_noalloc allocates nothing: pass o and lse")
+    B, H, Lq, Lk, D, o, lse = _check(q, k, v, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = [(ctypes.c_int64 * 3)(*t.stride()[:3]) for t in (q, k, v, o)]
+    code = lib.fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      B, H, Lq, Lk, D, *[ctypes.cast(s_, ctypes.c_void_p) for s_ in st],
+                                      float(scale), 1 if causal else 0, _DTYPES[q.dtype], int(num_splits),
+                                      stream.cuda_stream)
+    if code != 0:
+        raise FaError(code)
+    return o, lse
 
 
 def suggest_num_splits(B: int, H: int, Lq: int, Lk: int, D: int, causal: bool, num_cu: int = 256) -> int:

@@ -6,16 +6,26 @@
 // enqueues one launch on the caller's stream (two with key splits: partials, then
 // the merge; three for the backward pass: row statistics, dQ, then dK and dV).
 // No allocation, no synchronisation, no global mutable state apart from the
-// per-thread last HIP error and a per-thread cache of each device's CU count.
+// per-thread last HIP error, a per-thread cache of each device's CU count, and
+// the device address of each GPU's copy of the allocation-free entry point's
+// scratch array (looked up once per device).
 
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
 #include "fa355.h"
 #include "fa_bwd_kernel.hpp"
 #include "fa_fwd_kernel.hpp"
+
+// Partials of fa_fwd_splitkv_noalloc: a device global instead of a caller's
+// workspace, one copy per GPU, held until the process ends.  Host code never
+// passes this name to a kernel (on the host it only stands for the symbol); it
+// passes the device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -74,6 +84,33 @@ int cu_count() {
   return n;
 }
 
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (nullptr, with the HIP error kept, if the lookup fails).
+void* scratch_ptr() {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidDevice);
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ptrs[dev] = ptr;
+  }
+  return ptrs[dev];
+}
+
 // Dropout keep threshold T = round((1 - p)·256): 256 keeps everything (no
 // dropout), 0 (p too close to 1) and p outside [0, 1) are errors (-1 returned).
 int drop_threshold(float p) {
@@ -93,7 +130,7 @@ size_t ws_bytes(int B, int H, int Lq, int D, int splits) {
 int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk, int D,
         const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride, const int64_t* o_stride,
         float scale, int causal, int dtype, int splits, void* ws, size_t ws_size, fa_stream_t stream,
-        float dropout_p = 0.0f, uint64_t seed = 0) {
+        float dropout_p = 0.0f, uint64_t seed = 0, bool use_scratch = false) {
   if (!q || !k || !v || !o || !lse || !q_stride || !k_stride || !v_stride || !o_stride) return FA_ERR_NULL;
   if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
@@ -110,7 +147,9 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   const int drop_t = drop_threshold(dropout_p);
   if (drop_t < 0) return FA_ERR_DROPOUT;
   if (splits < 1 || splits > kMaxSplits) return FA_ERR_SPLITS;
-  if (splits > 1) {
+  if (splits > 1 && use_scratch) {
+    if (ws_bytes(B, H, Lq, D, splits) > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  } else if (splits > 1) {
     if (!ws) return FA_ERR_NULL;
     if (!aligned(ws, 256)) return FA_ERR_ALIGN;
     if (ws_size < ws_bytes(B, H, Lq, D, splits)) return FA_ERR_WORKSPACE;
@@ -141,6 +180,12 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   if (narrow) n_qt = ((int64_t)Lq + fa355::Geo<128, 4>::BR - 1) / fa355::Geo<128, 4>::BR;
   const int64_t num_wg = (int64_t)B * H * n_qt * splits;
   if ((int64_t)B * H >= (1ll << 31) || num_wg >= (1ll << 22)) return FA_ERR_SHAPE;
+
+  if (splits > 1 && use_scratch) {  // every argument is valid: now the one HIP query
+    ws = scratch_ptr();
+    if (!ws) return FA_ERR_DEVICE;
+    ws_size = FA_NOALLOC_SCRATCH_BYTES;
+  }
 
   fa355::FwdParams p;
   p.q = q;
@@ -347,6 +392,14 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
              num_splits, workspace, workspace_bytes, stream);
 }
 
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                           int Lk, int D, const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                           const int64_t* o_stride, float scale, int causal, int dtype, int num_splits,
+                           fa_stream_t stream) {
+  return fwd(q, k, v, o, lse, B, H, Lq, Lk, D, q_stride, k_stride, v_stride, o_stride, scale, causal, dtype,
+             num_splits, nullptr, 0, stream, 0.0f, 0, true);
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int Lq) {
   if (B < 1 || H < 1 || Lq < 1) return 0;
   return bwd_ws_bytes(B, H, Lq);
@@ -407,7 +460,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_STRIDE: return "fa_fwd: strides must be >= 0, with a row stride of at least D";
     case FA_ERR_SPLITS: return "fa_fwd_splitkv: num_splits must be between 1 and 256";
     case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1) with round((1 - p) * 256) >= 1";
-    case FA_ERR_WORKSPACE: return "workspace smaller than the size query returns (fa_fwd_splitkv / fa_bwd)";
+    case FA_ERR_WORKSPACE:
+      return "workspace smaller than the size query returns (fa_fwd_splitkv / fa_bwd), or partials larger than "
+             "the scratch array of fa_fwd_splitkv_noalloc";
     default: return "fa_fwd: unknown status code";
   }
 }
