@@ -6,6 +6,7 @@
     python bench.py --summarize-trace DIR    # kernel-trace stats CSV -> profiles/*_kernel_trace.md
     python bench.py --summarize-counters DIR # SQ counter CSVs -> profiles/*_sq_counters.md
     python bench.py --pass bwd [--workload W] # the backward pass (fa_bwd) instead of the forward
+    python bench.py --microbench             # MFMA, v_exp_f32, LDS and HBM rates of this GPU (libfa355_mb.so)
 
 One step = one ``fa_fwd`` call (the whole hot path: one kernel) over the
 workload's seeded synthetic Q, K, V, which are resident in HBM before timing
@@ -597,17 +598,102 @@ def run_timed(step, stream, steps: int, warmup: int, settle_s: float) -> dict:
                            "timed_mean": round(sum(samples) / len(samples)) if samples else None,
                            "timed_min": round(min(samples)) if samples else None,
                            "timed_max": round(max(samples)) if samples else None,
-                           "timed_samples": len(samples), "source": "amdsmi current_gfxclks" if clk else None}}
+                           "timed_samples": len(samples),
+                           "source": ("amdsmi current_gfxclks, mean over the XCDs; the driver refreshes it about "
+                                      "once a second, so after_settle and the timed samples show the clock the "
+                                      "settle phase's load brought the GPU to")}}
     return {"wall": wall, "ms": ms, "timing": timing}
 
 
 def at_clock(timing: dict, achieved_tflops: float) -> None:
     """Add the MFMA peak at the sampled shader clock and the fraction of it reached (in place)."""
-    c = timing["sclk_mhz"].get("timed_mean") or timing["sclk_mhz"].get("after")
+    c = timing["sclk_mhz"].get("timed_mean") or timing["sclk_mhz"].get("after_settle")
     if c:
         peak = PEAK_BF16_TFLOPS * c / 2400.0
         timing["peak_at_clock_tflops"] = round(peak, 1)
         timing["frac_of_peak_at_clock"] = round(achieved_tflops / peak, 4)
+
+
+def microbench(settle_s: float = 0.5) -> dict:
+    """The units' rates on this GPU (libfa355_mb.so): bf16 MFMA, v_exp_f32, LDS reads, HBM copy.
+
+    Each kernel is launched for settle_s seconds, then five launches of ~3-11 ms are timed with HIP events on
+    the stream (the best is reported).  The MFMA, exp and LDS kernels measure the shader clock themselves (cycle
+    counter against the 100 MHz real-time counter over a workgroup's lifetime); rates per CU and clock use it."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "tiled_attention_06_amd", "libfa355_mb.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} missing: build with python tiled_attention_06_amd/build.py")
+    lib = ctypes.CDLL(path)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    for name in ("mb_mfma", "mb_exp", "mb_lds"):
+        getattr(lib, name).argtypes = [vp, vp, i, i, vp, vp]
+        getattr(lib, name).restype = i
+    lib.mb_copy.argtypes = [vp, vp, ctypes.c_size_t, i, vp]
+    lib.mb_copy.restype = i
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device="cpu").manual_seed(5)
+    ops = (torch.randn(256 * 8, generator=g) * 0.5).to(torch.bfloat16).to(dev)          # 256 x 16 B of bf16
+    fsrc = torch.rand(256, generator=g).to(dev)
+    lsrc = torch.randint(0, 2 ** 31, (8192 * 4,), generator=g, dtype=torch.int32).to(dev)
+    nbytes = 1 << 30
+    csrc = torch.randint(0, 2 ** 31, (nbytes // 4,), dtype=torch.int32, device=dev)
+    cdst = torch.empty_like(csrc)
+    out = torch.empty(1024 * 512, dtype=torch.float32, device=dev)
+    cyc = torch.zeros(2, dtype=torch.int64, device=dev)   # shader cycles, 100 MHz ticks (kernels that measure)
+
+    def timed(launch, work, unit, per, measures_clock=True):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(4):
+                assert launch() == 0
+            torch.cuda.synchronize(dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        mhzs = []
+        for a, b in ev:
+            a.record(stream)
+            assert launch() == 0
+            b.record(stream)
+            if measures_clock:
+                torch.cuda.synchronize(dev)
+                c, t = (int(x) for x in cyc.tolist())
+                if t > 0:
+                    mhzs.append(100.0 * c / t)
+        torch.cuda.synchronize(dev)
+        sec = min(a.elapsed_time(b) for a, b in ev) / 1e3
+        mhz = sum(mhzs) / len(mhzs) if mhzs else None
+        rate = work / sec
+        r = {"rate": round(rate / per, 3), "unit": unit, "best_launch_ms": round(sec * 1e3, 3),
+             "sclk_mhz": round(mhz) if mhz else None}
+        if mhz:
+            r["per_cu_per_clock"] = round(rate / (cu * mhz * 1e6), 3)
+        return r
+
+    s_ = stream.cuda_stream
+    res = {"cu_count": cu}
+    it = 40000
+    cp = cyc.data_ptr()
+    res["mfma_bf16"] = timed(lambda: lib.mb_mfma(ops.data_ptr(), out.data_ptr(), 2 * cu, it, cp, s_),
+                             2 * cu * 4 * it * 8 * 2 * 32 * 32 * 16, "TFLOP/s", 1e12)
+    res["mfma_bf16"]["frac_of_spec_peak"] = round(res["mfma_bf16"]["rate"] / PEAK_BF16_TFLOPS, 4)
+    if res["mfma_bf16"].get("sclk_mhz"):
+        res["mfma_bf16"]["frac_of_peak_at_clock"] = round(
+            res["mfma_bf16"]["rate"] / (PEAK_BF16_TFLOPS * res["mfma_bf16"]["sclk_mhz"] / 2400.0), 4)
+    it = 20000
+    res["v_exp_f32"] = timed(lambda: lib.mb_exp(fsrc.data_ptr(), out.data_ptr(), 4 * cu, it, cp, s_),
+                             4 * cu * 256 * it * 8, "G exp/s", 1e9)
+    res["lds_read_b128"] = timed(lambda: lib.mb_lds(lsrc.data_ptr(), out.data_ptr(), cu, it, cp, s_),
+                                 cu * 8 * it * 8 * 1024, "TB/s", 1e12)
+    res["hbm_copy"] = timed(lambda: lib.mb_copy(csrc.data_ptr(), cdst.data_ptr(), nbytes, 16 * cu, s_),
+                            2 * nbytes, "GB/s", 1e9, measures_clock=False)
+    res["hbm_copy"]["frac_of_spec_peak"] = round(res["hbm_copy"]["rate"] / PEAK_HBM_GBS, 4)
+    assert torch.equal(csrc, cdst), "copy kernel result differs"
+    return res
 
 
 def bench_bwd(args, w) -> int:
@@ -697,6 +783,8 @@ def main() -> int:
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", metavar="DIR", help="SQ counter CSVs -> profiles/*_sq_counters.md")
     ap.add_argument("--bench-log", metavar="FILE", help="bench JSON line to quote in the trace summary")
+    ap.add_argument("--microbench", action="store_true",
+                    help="rates of the units on this GPU (MFMA, v_exp_f32, LDS, HBM copy) as one JSON line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -738,6 +826,9 @@ def main() -> int:
 
     if args.traffic_probe:
         traffic_probe(w, steps=3, pass_=args.pass_)
+        return 0
+    if args.microbench:
+        print(json.dumps({"microbench": microbench()}), flush=True)
         return 0
     if args.pass_ == "bwd":
         return bench_bwd(args, w)

@@ -1,4 +1,4 @@
-"""Build libfa355.so in-tree with hipcc for gfx950.
+"""Build libfa355.so (and the microbenchmark library libfa355_mb.so) in-tree with hipcc for gfx950.
 
 Usage: ``python tiled_attention_06_amd/build.py`` (or ``__graft_entry__.build()``).
 This file is run as a script or loaded by path: importing the package itself
@@ -18,6 +18,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "fa355.hip")
 OUT = os.path.join(PKG, "libfa355.so")
+# microbenchmarks of the units (bench.py --microbench): a library of its own, never loaded by the package
+MB_SRC = os.path.join(PKG, "csrc", "microbench.hip")
+MB_OUT = os.path.join(PKG, "libfa355_mb.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -44,10 +47,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfa355)")
 
 
-def build_library(out: str = OUT, verbose: bool = False) -> str:
+def build_library(out: str = OUT, verbose: bool = False, src: str = SRC) -> str:
     tmp = f"{out}.tmp{os.getpid()}"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           "-o", tmp, SRC]
+           "-o", tmp, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,5 +62,11 @@ def build_library(out: str = OUT, verbose: bool = False) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> list[str]:
+    """Every HIP library of the package: libfa355.so and the microbenchmarks' libfa355_mb.so."""
+    return [build_library(OUT, verbose, SRC), build_library(MB_OUT, verbose, MB_SRC)]
+
+
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv))
+    for path in build_all(verbose="-v" in sys.argv):
+        print(path)

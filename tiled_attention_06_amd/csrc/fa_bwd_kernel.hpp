@@ -261,30 +261,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const bool need_mask = (CAUSAL && j0 + BC - 1 > i0w + off) || (j0 + BC > Lk);
       const int lim_tail = Lk - j0 - 4 * g;
       const int lim = CAUSAL ? min(qrow + off - j0 - 4 * g + 1, lim_tail) : lim_tail;
-      // dropout words of the tile (blocks x = 4kb + 2h + a: keys 32kb + 16h + 8a + 4g + 0..3
-      // of row qrow; lane j of a quad computes blocks 2j, 2j + 1, the quad exchanges words)
-      uint32_t words[8];
-      if constexpr (DROP) {
-        const int j = lane & 3;
-        u32x4 mine[2];
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          const int x = 2 * j + sl, kb = x >> 2, h = (x >> 1) & 1, a = x & 1;
-          mine[sl] = drop_block((j0 + 32 * kb + 16 * h + 8 * a + 4 * g) >> 2, qrow >> 2, bh, p.seed_lo, p.seed_hi);
-        }
-#pragma unroll
-        for (int x = 0; x < 8; ++x) words[x] = quad_word(mine[x & 1], x >> 1, j);
-      }
       u32x4 db[KB][2];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb) {
+        // dropout words of the half kb (blocks x = 4kb + 2h + a: keys 32kb + 16h + 8a + 4g
+        // + 0..3 of row qrow; lane j of a quad computes block 4kb + j, the quad transposes)
+        uint32_t wd[4] = {0u, 0u, 0u, 0u};
+        if constexpr (DROP) {
+          const int j = lane & 3;
+          const u32x4 mine =
+              drop_block((j0 + 32 * kb + 16 * (j >> 1) + 8 * (j & 1) + 4 * g) >> 2, qrow >> 2, bh, p.seed_lo,
+                         p.seed_hi);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wd[i] = mine[i];
+          quad_transpose(wd, j);
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           // dropout words of registers 8h..8h+7
           uint32_t dwd[2] = {0u, 0u};
           if constexpr (DROP) {
-            dwd[0] = words[4 * kb + 2 * h];
-            dwd[1] = words[4 * kb + 2 * h + 1];
+            dwd[0] = wd[2 * h];
+            dwd[1] = wd[2 * h + 1];
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -308,6 +306,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             db[kb][h][e] = pack2<DT>(ds[0], ds[1]);
           }
         }
+      }
       // dQᵀ += Kᵀ·dSᵀ: A = 8 keys of one head dim (two transposing reads)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)

@@ -116,17 +116,19 @@ struct FwdParams {
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
 // as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit products, the high
 // halves xored into the other two words with the key, and the key advanced by
-// the Weyl constants between rounds.
+// the Weyl constants between rounds.  Each product is written as one 64-bit
+// multiply, which gfx950 does in a single v_mad_u64_u32 (both halves) instead of
+// a v_mul_lo_u32 and a v_mul_hi_u32 (all of them quarter-rate instructions).
 __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                           uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = c0 * 0xD2511F53u, hi0 = __umulhi(c0, 0xD2511F53u);
-    const uint32_t lo1 = c2 * 0xCD9E8D57u, hi1 = __umulhi(c2, 0xCD9E8D57u);
-    c0 = hi1 ^ c1 ^ k0;
-    c1 = lo1;
-    c2 = hi0 ^ c3 ^ k1;
-    c3 = lo0;
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    c1 = (uint32_t)p1;
+    c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -153,11 +155,26 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t w, int s) {
     default: return quad_bcast_c<3>(w);
   }
 }
-// Word j of lane s's block x, for lane j of each quad (j = lane & 3)
-__device__ __forceinline__ uint32_t quad_word(const u32x4& x, int s, int j) {
-  const uint32_t w0 = quad_bcast(x[0], s), w1 = quad_bcast(x[1], s), w2 = quad_bcast(x[2], s),
-                 w3 = quad_bcast(x[3], s);
-  return j == 0 ? w0 : j == 1 ? w1 : j == 2 ? w2 : w3;
+// 4 x 4 transpose within each quad of lanes (j = lane & 3): lane j holds v[0..3],
+// the four words of one Philox block; afterwards v[s] is word j of the block lane
+// s held.  Two butterfly stages (partners j^1, then j^2); in each, a lane sends
+// the element of every register pair it does not keep and takes its partner's.
+__device__ __forceinline__ void quad_transpose(uint32_t (&v)[4], int j) {
+  const bool b0 = (j & 1) != 0, b1 = (j & 2) != 0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {  // pairs (0,1), (2,3); quad_perm(1,0,3,2)
+    const uint32_t send = b0 ? v[2 * q] : v[2 * q + 1];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xf, 0xf, false);
+    v[2 * q] = b0 ? recv : v[2 * q];
+    v[2 * q + 1] = b0 ? v[2 * q + 1] : recv;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {  // pairs (0,2), (1,3); quad_perm(2,3,0,1)
+    const uint32_t send = b1 ? v[q] : v[q + 2];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0x4E, 0xf, 0xf, false);
+    v[q] = b1 ? recv : v[q];
+    v[q + 2] = b1 ? v[q + 2] : recv;
+  }
 }
 
 // 16-bit lane masks of the kept weights of word w's bytes b0 and b0+1
@@ -544,30 +561,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // With DROP, the weights that multiply V are masked by the dropout bits of
   // their (row, key); the sums stay those of all weights (dropout acts on the
   // normalised weights, and LSE is that of the scores).
-  // Dropout words of a tile: the lane needs, for blocks x = 4kb + 2h + a (keys
-  // 32kb + 16h + 8a + 4g + 0..3 of its row), word row % 4.  The four lanes of a
-  // quad share the row block, so lane j computes blocks 2j and 2j + 1 and the
-  // quad exchanges words (one Philox call per four elements becomes one per 16).
-  auto drop_tile = [&](int t, uint32_t (&words)[8]) {
+  // Dropout words of one 32-key half kb of a tile: the lane needs, for blocks
+  // x = 4kb + 2h + a (keys 32kb + 16h + 8a + 4g + 0..3 of its row), word row % 4.
+  // The four lanes of a quad share the row block, so lane j computes block
+  // 4kb + j and the quad transposes the words (one Philox call per four elements
+  // becomes one per 16); wd[2h + a] is then this lane's word of block 4kb + 2h + a.
+  auto drop_words = [&](int t, int kb, uint32_t (&wd)[4]) {
     const int lane_d = opaque(tid) & 63;
     const int row_d = i0w + (lane_d & 31), g_d = lane_d >> 5, j = lane_d & 3;
-    u32x4 mine[2];
+    const u32x4 mine = drop_block((t * BC + 32 * kb + 16 * (j >> 1) + 8 * (j & 1) + 4 * g_d) >> 2, row_d >> 2,
+                                  bh, p.seed_lo, p.seed_hi);
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      const int x = 2 * j + sl, kb = x >> 2, h = (x >> 1) & 1, a = x & 1;
-      mine[sl] = drop_block((t * BC + 32 * kb + 16 * h + 8 * a + 4 * g_d) >> 2, row_d >> 2, bh, p.seed_lo,
-                            p.seed_hi);
-    }
-#pragma unroll
-    for (int x = 0; x < 8; ++x) words[x] = quad_word(mine[x & 1], x >> 1, j);
+    for (int i = 0; i < 4; ++i) wd[i] = mine[i];
+    quad_transpose(wd, j);
   };
   auto make_p = [&](const f32x16(&S)[KB], u32x4(&pb)[KB][2], int t) {
     const float mb = m_run;
     float sf = 0.f, sr = 0.f;
-    uint32_t words[8];
-    if constexpr (DROP) drop_tile(t, words);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
+      uint32_t wd[4];
+      if constexpr (DROP) drop_words(t, kb, wd);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // keys of registers 8h..8h+7: 32kb + 16h + 4g + {0..3} and + 8 + 4g + {0..3}
@@ -575,7 +589,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if constexpr (DROP) {
 #pragma unroll
           for (int a = 0; a < 2; ++a) {
-            const uint32_t w = words[4 * kb + 2 * h + a];
+            const uint32_t w = wd[2 * h + a];
             dw[a] = u32x4{keep_pair(w, 0, p.drop_t), keep_pair(w, 2, p.drop_t), 0u, 0u};
           }
         }
@@ -592,6 +606,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             pb[kb][h][e] = pk;
         }
       }
+    }
     l_f += sf;
     l_r += sr;
   };
@@ -659,6 +674,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         copy_v(t + G::NS - 1, PC{});
       }
       if (live) {
+        // LLVM's interleave strategy for small-GEMM bodies (MFMAs spaced between the
+        // LDS operand reads and the VALU work): 1.8% faster on the 7B 4K shape than
+        // the default schedule, same results
+        __builtin_amdgcn_iglp_opt(0);
         compute_s(kst(PN{}), Sn);
         u32x4 pb[KB][2];
         make_p(Sc, pb, t);
