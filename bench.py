@@ -14,8 +14,8 @@ starts.  The metric is attention-forward TFLOP/s with FLOP = 4·B·H·Lq·Lk·D,
 halved for causal, and its fraction of MI355X's dense bf16 MFMA peak.  The
 split-KV inference shapes (``--workload kvcache_16k`` and the like) step through
 ``fa_fwd_splitkv`` (main kernel plus merge); those below the ridge point report
-an HBM roofline instead.  ``--pass bwd`` times ``fa_bwd`` (row statistics, dQ,
-then dK/dV kernels) with o and lse from ``fa_fwd`` computed before timing and a
+an HBM roofline instead.  ``--pass bwd`` times ``fa_bwd`` (the dQ kernel, which
+also forms the row statistics, then the dK/dV kernel) with o and lse from ``fa_fwd`` computed before timing and a
 seeded upstream gradient; its FLOP are 2.5x the forward's (five products of the
 same shape instead of two: the usual count for a recomputing backward pass).
 
@@ -318,7 +318,7 @@ def summarize_traffic(directory: str, w, pass_: str = "fwd") -> str:
     per = {}
     for r in rows:
         per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
-    ours = ("fa_fwd_kernel",) if pass_ == "fwd" else ("fa_bwd_prep_kernel", "fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel")
+    ours = ("fa_fwd_kernel",) if pass_ == "fwd" else ("fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel")
     mine = {name: [c for (kn, _), c in per.items() if name in kn] for name in ours}
     if not all(mine.values()):
         raise SystemExit(f"no dispatches of {[n for n, c in mine.items() if not c]} in the counter CSVs")
@@ -746,8 +746,7 @@ def bench_bwd(args, w) -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
                      "traffic": committed_traffic(w.name, "bwd") if not args.dropout else None,
-                     "kernel": "fa_bwd_prep_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (the events bracket all "
-                               "three)", "mean_launch_us": round(mean_s * 1e6, 3)},
+                     "kernel": "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (the events bracket both)", "mean_launch_us": round(mean_s * 1e6, 3)},
         "timing": res["timing"],
     }
     at_clock(out["timing"], achieved)

@@ -218,8 +218,9 @@ int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
  * dq, dk, dv must not overlap each other or the inputs.  q, k, v, o, dout, dq,
  * dk, dv must be 16-byte aligned (FA_ERR_ALIGN), lse 4-byte aligned.  Every
  * pointer is required (FA_ERR_NULL).  Limits: (L + 256)*D*2 < 2^32 bytes for
- * L = Lq and L = Lk (FA_ERR_SHAPE).  Three kernels are enqueued (row
- * statistics, dq, then dk and dv); the call returns without synchronising.
+ * L = Lq and L = Lk (FA_ERR_SHAPE).  Two kernels are enqueued (dq, which
+ * also writes every row's D_i and lse_i*log2(e) to the workspace, then dk and
+ * dv, which read them); the call returns without synchronising.
  * Precision: fp32 accumulation; P and dS are rounded to `dtype` as matrix-core
  * operands.  Each output element is written by exactly one thread, in a fixed
  * order, so results are bitwise reproducible.

@@ -4,7 +4,7 @@
 // FA_ERR_* of a bad argument can be produced without a GPU.  A valid call
 // selects the kernel instance for (head dim, dtype, causal, workgroup size) and
 // enqueues one launch on the caller's stream (two with key splits: partials, then
-// the merge; three for the backward pass: row statistics, dQ, then dK and dV).
+// the merge; two for the backward pass: dQ with the row statistics, then dK and dV).
 // No allocation, no synchronisation, no global mutable state apart from the
 // per-thread last HIP error, a per-thread cache of each device's CU count, and
 // the device address of each GPU's copy of the allocation-free entry point's
@@ -52,8 +52,17 @@ int launch(const fa355::FwdParams& p, const fa355::MergeParams& m, hipStream_t s
   if (st != FA_OK || p.n_split == 1) return st;
   constexpr int rows_per_block = 256 / (D / 4);
   const int64_t rows = (int64_t)m.bh * m.Lq;
-  hipLaunchKernelGGL((fa355::fa_merge_kernel<D, DT>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                     dim3(256), 0, stream, m);
+  const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
+  // splits merged per batch of loads: as many as there are, up to 16 (a batch
+  // larger than the split count only adds predicated-off slots and registers)
+  if (m.n_split <= 2)
+    hipLaunchKernelGGL((fa355::fa_merge_kernel<D, DT, 2>), grid, dim3(256), 0, stream, m);
+  else if (m.n_split <= 4)
+    hipLaunchKernelGGL((fa355::fa_merge_kernel<D, DT, 4>), grid, dim3(256), 0, stream, m);
+  else if (m.n_split <= 8)
+    hipLaunchKernelGGL((fa355::fa_merge_kernel<D, DT, 8>), grid, dim3(256), 0, stream, m);
+  else
+    hipLaunchKernelGGL((fa355::fa_merge_kernel<D, DT, 16>), grid, dim3(256), 0, stream, m);
   return launch_status();
 }
 
@@ -260,16 +269,12 @@ size_t bwd_ws_bytes(int B, int H, int Lq) {
 
 template <int D, int DT, bool CAUSAL, bool DROP>
 int launch_bwd(fa355::BwdParams p, hipStream_t stream) {
-  constexpr int rows_per_block = 256 / (D / 8);
-  const int64_t rows = (int64_t)p.bh * p.Lq4;
-  hipLaunchKernelGGL((fa355::fa_bwd_prep_kernel<D, DT>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                     dim3(256), 0, stream, p);
-  int st = launch_status();
-  if (st != FA_OK) return st;
+  // the dQ kernel also writes each row's Δ and LSE·log2(e) to the workspace, which
+  // the dK/dV kernel (next on the stream) reads
   p.num_wg = p.bh * p.n_qt;
   p.xcd_remap = (p.num_wg % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((fa355::fa_bwd_dq_kernel<D, DT, CAUSAL, DROP>), dim3(p.num_wg), dim3(512), 0, stream, p);
-  st = launch_status();
+  int st = launch_status();
   if (st != FA_OK) return st;
   p.num_wg = p.bh * p.n_kt;
   p.xcd_remap = (p.num_wg % 8 == 0) ? 1 : 0;

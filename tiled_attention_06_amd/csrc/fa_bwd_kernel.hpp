@@ -12,11 +12,11 @@
 //   dV_j = Σ_i P_ij dO_i,  dP_ij = dO_i·v_j,  Δ_i = Σ_j P_ij dP_ij = dO_i·O_i,
 //   dS_ij = P_ij (dP_ij − Δ_i),  dQ_i = scale Σ_j dS_ij k_j,  dK_j = scale Σ_i dS_ij q_i.
 //
-// Three kernels on one stream:
-//   * fa_bwd_prep_kernel: per row, Δ = dO·O (fp32 from the stored values) and
-//     LSE·log2(e), into the workspace;
+// Two kernels on one stream:
 //   * fa_bwd_dq_kernel: one workgroup = 8 waves = 256 query rows (as the forward
-//     pass); per 64-key tile Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ on MFMA (Q and dO rows
+//     pass); each lane first forms its row's Δ = dO·O (fp32 from the stored
+//     values) and LSE·log2(e) and writes both to the workspace for the second
+//     kernel; per 64-key tile Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ on MFMA (Q and dO rows
 //     resident in VGPRs as B operands), P and dS in registers (one row per lane),
 //     dQᵀ += Kᵀ·dSᵀ with Kᵀ read through transposing LDS reads;
 //   * fa_bwd_dkdv_kernel: one workgroup = 4 waves = 128 keys, each wave owns 32
@@ -94,40 +94,6 @@ __device__ __forceinline__ float2 unpack2(uint32_t u) {
   else
     return make_float2((float)__builtin_bit_cast(_Float16, (unsigned short)(u & 0xffffu)),
                        (float)__builtin_bit_cast(_Float16, (unsigned short)(u >> 16)));
-}
-
-// Δ_i = Σ_d dO_id·O_id and LSE_i·log2(e), per head padded with zero rows to Lq4.
-// D/8 lanes per row, 16-byte loads.
-template <int D, int DT>
-__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR;
-  const int tid = threadIdx.x;
-  const int64_t w = (int64_t)blockIdx.x * RPB + tid / LPR;  // row over B*H*Lq4
-  const int c0 = (tid % LPR) * 8;
-  const int64_t total = (int64_t)p.bh * p.Lq4;
-  const int64_t bh = w / p.Lq4, i = w - bh * p.Lq4;
-  const bool real = w < total && i < p.Lq;
-  const int64_t r = bh * p.Lq + i;  // the row in lse
-  float acc = 0.f;
-  if (real) {
-    const char* orow = bwd_slab((const char*)p.o, p, T_O, (int)bh) + (i * p.sl[T_O] + c0) * 2;
-    const char* drow = bwd_slab((const char*)p.dout, p, T_DO, (int)bh) + (i * p.sl[T_DO] + c0) * 2;
-    const u32x4 a = *(const u32x4*)orow;
-    const u32x4 b = *(const u32x4*)drow;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float2 x = unpack2<DT>(a[e]), y = unpack2<DT>(b[e]);
-      acc = __builtin_fmaf(x.x, y.x, acc);
-      acc = __builtin_fmaf(x.y, y.y, acc);
-    }
-  }
-  // sum over the LPR lanes of the row (aligned groups within the wave)
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (w < total && tid % LPR == 0) {
-    p.ws_delta[w] = acc;
-    p.ws_lse2[w] = real ? p.lse[r] * 1.44269504088896340736f : 0.f;
-  }
 }
 
 // Tile copies HBM -> LDS for the backward kernels: a tile of 64 rows of one
@@ -222,9 +188,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     qr[s] = buf_load16(qrs, (uint32_t)(qrow * p.sl[T_Q] + 16 * s + 8 * g) * 2);
     dr[s] = buf_load16(dors, (uint32_t)(qrow * p.sl[T_DO] + 16 * s + 8 * g) * 2);
   }
+  // Δ = dO·O of the lane's row from the stored O (fp32, this lane's half of the
+  // head dims, then the other half-wave's), and LSE·log2(e); both are also written
+  // to the workspace for the dK/dV kernel, with zeros for the padding rows
+  // Lq..Lq4-1 (rows past Lq read O = dO = 0 through the buffer range)
   const bool row_ok = qrow < Lq;
-  const float lse2 = row_ok ? p.ws_lse2[(int64_t)bh * p.Lq4 + qrow] : 0.f;
-  const float delta = row_ok ? p.ws_delta[(int64_t)bh * p.Lq4 + qrow] : 0.f;
+  float delta = 0.f;
+  {
+    const char* const oslab = bwd_slab((const char*)p.o, p, T_O, bh);
+    const auto ors = make_rsrc(oslab, bwd_end<D>(p, T_O, Lq));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 ov = buf_load16(ors, (uint32_t)(qrow * p.sl[T_O] + 16 * s + 8 * g) * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 x = unpack2<DT>(ov[e]), y = unpack2<DT>(dr[s][e]);
+        delta = __builtin_fmaf(x.x, y.x, delta);
+        delta = __builtin_fmaf(x.y, y.y, delta);
+      }
+    }
+    delta = xhalf_sum(delta);
+  }
+  const float lse2 = row_ok ? p.lse[(int64_t)bh * Lq + qrow] * 1.44269504088896340736f : 0.f;
+  if (g == 0 && qrow < p.Lq4) {
+    p.ws_lse2[(int64_t)bh * p.Lq4 + qrow] = lse2;
+    p.ws_delta[(int64_t)bh * p.Lq4 + qrow] = delta;
+  }
   const float c = p.c;
 
   auto row_off = [](int rows, int BS) { return (rows % NBLK) * BS + (rows / NBLK) * 2 * D; };
@@ -261,21 +250,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const bool need_mask = (CAUSAL && j0 + BC - 1 > i0w + off) || (j0 + BC > Lk);
       const int lim_tail = Lk - j0 - 4 * g;
       const int lim = CAUSAL ? min(qrow + off - j0 - 4 * g + 1, lim_tail) : lim_tail;
-      u32x4 db[KB][2];
+      // dropout words of the tile: lane j of a quad computes blocks 4kb + j for both halves kb,
+      // the quad transposes each half's words
+      uint32_t words[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      if constexpr (DROP) {
+        const int j = lane & 3;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        // dropout words of the half kb (blocks x = 4kb + 2h + a: keys 32kb + 16h + 8a + 4g
-        // + 0..3 of row qrow; lane j of a quad computes block 4kb + j, the quad transposes)
-        uint32_t wd[4] = {0u, 0u, 0u, 0u};
-        if constexpr (DROP) {
-          const int j = lane & 3;
+        for (int kb = 0; kb < KB; ++kb) {
           const u32x4 mine =
               drop_block((j0 + 32 * kb + 16 * (j >> 1) + 8 * (j & 1) + 4 * g) >> 2, qrow >> 2, bh, p.seed_lo,
                          p.seed_hi);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) wd[i] = mine[i];
+          uint32_t wd[4] = {mine[0], mine[1], mine[2], mine[3]};
           quad_transpose(wd, j);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) words[4 * kb + i] = wd[i];
         }
+      }
+      u32x4 db[KB][2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        uint32_t* wd = words + 4 * kb;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           // dropout words of registers 8h..8h+7

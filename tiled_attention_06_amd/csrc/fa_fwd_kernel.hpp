@@ -636,7 +636,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-
   auto kst_rt = [&](int st) -> unsigned char* { return st == 0 ? ks0 : st == 1 ? ks1 : st == 2 ? ks2 : ks3; };
   auto vst_rt = [&](int st) -> unsigned char* { return st == 0 ? vs0 : st == 1 ? vs1 : st == 2 ? vs2 : vs3; };
   // K and V of tile t+NS-1, copied in iteration t into the stage of tile t-1,
@@ -776,8 +775,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // i with split partials (Ô_s, m_s, lf_s, lr_s), all relative to m_s in log2 units:
 //   M = max_s m_s,  w_s = 2^(m_s - M),
 //   O = Σ w_s Ô_s / Σ w_s lr_s,   LSE = (M + log2 Σ w_s lf_s) · ln 2,
-// which is what one pass over all keys computes.  HBM-bound; one row per D/4
-// lanes, 4 dims per lane.
+// which is what one pass over all keys computes.  One pass over the splits in
+// batches of MB (2..16, the launcher's pick for the split count): the loads of a
+// batch are issued together (a serial loop would
+// pay one memory round trip per split, which dominated decode steps with many
+// splits), the running max moves to the batch's max and the sums are rescaled
+// by 2^(M_old - M_new) — the streaming update once more.  HBM-bound; one row per
+// D/4 lanes, 4 dims per lane.
 struct MergeParams {
   const float* ws_o;
   const float* ws_ml;
@@ -788,7 +792,7 @@ struct MergeParams {
   int o_sl;
 };
 
-template <int D, int DT>
+template <int D, int DT, int MB>
 __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
   constexpr int LPR = D / 4, RPB = 256 / LPR;
   const int tid = threadIdx.x;
@@ -797,25 +801,43 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
   if (r >= (int64_t)p.bh * p.Lq) return;
   const int bh = (int)(r / p.Lq), i = (int)(r - (int64_t)bh * p.Lq);
   const size_t stride = (size_t)p.bh * p.Lq;  // rows per split
-  float M = -3.0e38f;
-  for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, p.ws_ml[((size_t)s * stride + r) * 4]);
-  float lf = 0.f, lr = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int s = 0; s < p.n_split; ++s) {
-    const size_t row = (size_t)s * stride + r;
-    const f32x4 st = *(const f32x4*)(p.ws_ml + row * 4);
-    const float w = __builtin_amdgcn_exp2f(st[0] - M);
-    lf += w * st[1];
-    lr += w * st[2];
-    const f32x4 x = *(const f32x4*)(p.ws_o + row * D + d0);
-    a0 += w * x[0];
-    a1 += w * x[1];
-    a2 += w * x[2];
-    a3 += w * x[3];
+  // M starts below every split's max (an empty split keeps -1e30): the first
+  // batch's scale 2^(M - M_new) is then 0 and the zero sums stay zero
+  float M = -3.0e38f, lf = 0.f, lr = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < p.n_split; s0 += MB) {
+    f32x4 st[MB], x[MB];
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      if (s0 + u < p.n_split) {
+        const size_t row = (size_t)(s0 + u) * stride + r;
+        st[u] = *(const f32x4*)(p.ws_ml + row * 4);
+        x[u] = *(const f32x4*)(p.ws_o + row * D + d0);
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < MB; ++u)
+      if (s0 + u < p.n_split) Mn = fmaxf(Mn, st[u][0]);
+    const float sc = __builtin_amdgcn_exp2f(M - Mn);
+    M = Mn;
+    lf *= sc;
+    lr *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      if (s0 + u < p.n_split) {
+        const float w = __builtin_amdgcn_exp2f(st[u][0] - M);
+        lf += w * st[u][1];
+        lr += w * st[u][2];
+        acc += w * x[u];
+      }
+    }
   }
   const float inv = 1.0f / lr;
   const int b = bh / p.H, h = bh - b * p.H;
   char* const orow = (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)i * p.o_sl + d0) * 2;
-  *(u32x2*)orow = u32x2{pack2<DT>(a0 * inv, a1 * inv), pack2<DT>(a2 * inv, a3 * inv)};
+  *(u32x2*)orow = u32x2{pack2<DT>(acc[0] * inv, acc[1] * inv), pack2<DT>(acc[2] * inv, acc[3] * inv)};
   if (d0 == 0) p.lse[r] = (M + log2f(lf)) * 0.69314718055994530942f;
 }
 
