@@ -360,9 +360,10 @@ def summarize_traffic(directory: str, w, pass_: str = "fwd") -> str:
         "",
         "Commands (from the repository root on the GPU box):",
         "",
-        f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic_fetch -o t -- python3 bench.py {probe}",
-        f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic_write -o t -- python3 bench.py {probe}",
-        f"    python3 bench.py{' --pass bwd' if pass_ == 'bwd' else ''} --summarize-traffic gpurun_out  (reads both directories)",
+        f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {directory}/traffic_fetch -o t -- python3 bench.py {probe}",
+        f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {directory}/traffic_write -o t -- python3 bench.py {probe}",
+        f"    python3 bench.py{' --pass bwd' if pass_ == 'bwd' else ''} --summarize-traffic {directory}  (reads both; "
+        "nothing else under that directory)",
         "",
         f"calibration: FETCH_SIZE {sum(cf) / len(cf):.1f} KiB (mean of {len(cf)}), WRITE_SIZE "
         f"{sum(cw) / len(cw):.1f} KiB (mean of {len(cw)}) for {COPY_BYTES / 1024:.0f} KiB moved -> "
@@ -431,10 +432,10 @@ def summarize_counters(directory: str, w) -> str:
         "",
     ]
     for i, p_ in enumerate(SQ_PASSES):
-        lines.append(f"    rocprofv3 --pmc {p_} --output-format csv -d gpurun_out/sq{i} -o sq -- python3 bench.py "
+        lines.append(f"    rocprofv3 --pmc {p_} --output-format csv -d {directory}/sq{i} -o sq -- python3 bench.py "
                      "--traffic-probe")
     lines += [
-        "    python3 bench.py --summarize-counters gpurun_out  (reads the three directories)",
+        f"    python3 bench.py --summarize-counters {directory}  (reads the three directories)",
         "",
         "Raw means per dispatch:",
         "",
@@ -484,8 +485,8 @@ def summarize_trace(directory: str, w, bench_line: str | None, pass_: str = "fwd
         "",
         "Command (from the repository root on the GPU box):",
         "",
-        f"    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o t -- python3 bench.py{run_args} --no-cpu-baseline --no-parity",
-        f"    python3 bench.py{wl} --summarize-trace gpurun_out/trace --bench-log <that run's stdout>",
+        f"    rocprofv3 --kernel-trace --stats --output-format csv -d {directory} -o t -- python3 bench.py{run_args} --no-cpu-baseline --no-parity",
+        f"    python3 bench.py{wl} --summarize-trace {directory} --bench-log <that run's stdout>",
         "",
         "(fa_fwd_kernel rows in a backward trace are the one forward call that makes o and lse.)" if pass_ == "bwd"
         else "",
