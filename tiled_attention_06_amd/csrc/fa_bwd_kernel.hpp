@@ -232,6 +232,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int j0 = t * BC;
     const bool active = !CAUSAL || j0 <= i0w + 31 + off;  // wave-uniform
     if (active) {
+      // LLVM's single-wave MFMA interleave strategy for this body: 3.9% faster on the
+      // 7B 4K shape than the default schedule, same results
+      __builtin_amdgcn_iglp_opt(1);
       const unsigned char* krb = st ? kr1 : kr0;
       const unsigned char* ktb = st ? kt1 : kt0;
       const unsigned char* vrb = st ? vr1 : vr0;
