@@ -119,15 +119,27 @@ struct FwdParams {
 // the Weyl constants between rounds.  Each product is written as one 64-bit
 // multiply, which gfx950 does in a single v_mad_u64_u32 (both halves) instead of
 // a v_mul_lo_u32 and a v_mul_hi_u32 (all of them quarter-rate instructions).
+// With B3, from the second round on each three-way xor is one v_bitop3_b32
+// (truth table 0x96: odd parity).  The first round keeps plain xors: there the
+// counter words and the key can all be uniform, and a VOP3 instruction reads at
+// most one scalar register, so a bitop3 would need a register copy; plain xors
+// let the scalar unit take the uniform part.  (Callers whose registers are
+// tightest — the dropout forward's masked tiles and its last full tile — take
+// B3 = false: the bitop3 schedule ran those paths out of registers.)  Same bits
+// either way.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+template <bool B3 = true>
 __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                           uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
     const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
-    c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    c0 = (r == 0 || !B3) ? (uint32_t)(p1 >> 32) ^ c1 ^ k0 : xor3((uint32_t)(p1 >> 32), c1, k0);
     c1 = (uint32_t)p1;
-    c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c2 = (r == 0 || !B3) ? (uint32_t)(p0 >> 32) ^ c3 ^ k1 : xor3((uint32_t)(p0 >> 32), c3, k1);
     c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
@@ -138,8 +150,9 @@ __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2,
 // Dropout bits of a 4 x 4 block of (query row, key) of one (batch, head): the
 // counter is (key / 4, row / 4, batch*head, 0); output word w, byte b covers row
 // 4*(row/4) + w and key 4*(key/4) + b.  A weight is kept iff its byte < T.
+template <bool B3 = true>
 __device__ __forceinline__ u32x4 drop_block(int key4, int row4, int bh, uint32_t k0, uint32_t k1) {
-  return philox10((uint32_t)key4, (uint32_t)row4, (uint32_t)bh, 0u, k0, k1);
+  return philox10<B3>((uint32_t)key4, (uint32_t)row4, (uint32_t)bh, 0u, k0, k1);
 }
 // Word w (the same register in every lane) of lane s of each quad of lanes
 // (quad_perm(s, s, s, s); s is a constant wherever the callers are unrolled).
@@ -566,22 +579,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // The four lanes of a quad share the row block, so lane j computes block
   // 4kb + j and the quad transposes the words (one Philox call per four elements
   // becomes one per 16); wd[2h + a] is then this lane's word of block 4kb + 2h + a.
-  auto drop_words = [&](int t, int kb, uint32_t (&wd)[4]) {
+  auto drop_words = [&](int t, int kb, uint32_t (&wd)[4], auto B3c) {
     const int lane_d = opaque(tid) & 63;
     const int row_d = i0w + (lane_d & 31), g_d = lane_d >> 5, j = lane_d & 3;
-    const u32x4 mine = drop_block((t * BC + 32 * kb + 16 * (j >> 1) + 8 * (j & 1) + 4 * g_d) >> 2, row_d >> 2,
-                                  bh, p.seed_lo, p.seed_hi);
+    const u32x4 mine = drop_block<decltype(B3c)::value>(
+        (t * BC + 32 * kb + 16 * (j >> 1) + 8 * (j & 1) + 4 * g_d) >> 2, row_d >> 2, bh, p.seed_lo, p.seed_hi);
 #pragma unroll
     for (int i = 0; i < 4; ++i) wd[i] = mine[i];
     quad_transpose(wd, j);
   };
-  auto make_p = [&](const f32x16(&S)[KB], u32x4(&pb)[KB][2], int t) {
+  // (B3c: std::true_type or std::false_type, the generator form for drop_words)
+  auto make_p = [&](const f32x16(&S)[KB], u32x4(&pb)[KB][2], int t, auto B3c) {
     const float mb = m_run;
     float sf = 0.f, sr = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       uint32_t wd[4];
-      if constexpr (DROP) drop_words(t, kb, wd);
+      if constexpr (DROP) drop_words(t, kb, wd, B3c);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // keys of registers 8h..8h+7: 32kb + 16h + 4g + {0..3} and + 8 + 4g + {0..3}
@@ -679,7 +693,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         __builtin_amdgcn_iglp_opt(0);
         compute_s(kst(PN{}), Sn);
         u32x4 pb[KB][2];
-        make_p(Sc, pb, t);
+        make_p(Sc, pb, t, std::true_type{});
         pv(pb, vst(Pc));
         mxn = row_max(Sn);
       }
@@ -699,7 +713,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (tf + G::NS - 1 < t_e) copies_rt(tf);
       if (live) {
         u32x4 pb[KB][2];
-        make_p(Sc, pb, tf);
+        make_p(Sc, pb, tf, std::false_type{});
         pv(pb, vst_rt((tf - t_b) % G::NS));
       }
       end_iter(tf);
@@ -722,7 +736,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       mask_tile(sA, t);
       const bool any = move_max(row_max(sA));
       u32x4 pb[KB][2];
-      make_p(sA, pb, t);
+      make_p(sA, pb, t, std::false_type{});
       scale_o(any);
       __builtin_amdgcn_sched_barrier(0);
       pv(pb, vst_rt((t - t_b) % G::NS));
