@@ -143,9 +143,9 @@ def test_edge_shapes(B, H, Lq, Lk, D, dtype, causal):
     compare(o, lse, O_ref, L_ref, dtype, "edge", src=inp)
 
 
-# Grids of 256-row workgroups larger than the CU count (256 on MI355X) run 8 waves per
-# workgroup; smaller ones (every case above) run 4 waves and 128 rows.  These cases keep
-# ragged tails and both sides of that boundary covered for the 8-wave form.
+# Grids of 256-row workgroups larger than the CU count (256 on MI355X) run that form; smaller
+# ones (every case above) run 128-row workgroups whose 8 waves form two key groups.  These cases
+# keep ragged tails and both sides of that boundary covered for the 256-row form.
 WIDE = [(1, 300, 300, 300, 64, "fp16", True), (1, 300, 300, 300, 128, "bf16", False),
         (2, 130, 129, 1000, 128, "bf16", False), (1, 257, 65, 65, 64, "bf16", True),
         (1, 256, 65, 65, 128, "fp16", True), (1, 257, 65, 65, 128, "fp16", True),
@@ -164,17 +164,30 @@ def test_wide_grids(B, H, Lq, Lk, D, dtype, causal):
 
 
 @pytest.mark.parametrize("D,dtype,causal", [(128, "bf16", True), (64, "fp16", False), (128, "fp16", False)])
-def test_geometry_bitwise(D, dtype, causal):
-    # 300 heads of 520 rows (3 query tiles of 256: 900 workgroups, the 8-wave form) against the
-    # first 4 heads alone (12 workgroups, the 4-wave form): every row is computed the same way in
-    # either grouping, so the two must agree bit for bit
+def test_geometry_forms(D, dtype, causal):
+    # 300 heads of 520 rows (3 query tiles of 256: 900 workgroups, the 256-row form) and the first 4
+    # heads alone (12 workgroups of 128 rows: the two-key-group form) both against the oracle on
+    # those heads.  Within one form a row does not depend on the rest of the grid: the first 296
+    # heads (888 workgroups, whose count lets the XCD-aware order run) and the first 8 heads (24
+    # workgroups) must reproduce the larger launches bit for bit.
     inp = ai.make_custom(1, 300, 520, 520, D, dtype, causal, seed=31_000 + D)
     note(f"geometry B1 H300 L520 D{D} {dtype} causal={causal}")
+    sub = lambda n: {**inp, **{x: inp[x][:, :n].contiguous() for x in ("q", "k", "v")}}
     o_all, l_all = run_gpu(inp)
-    few = {n: inp[n][:, :4].contiguous() for n in ("q", "k", "v")}
-    o_few, l_few = run_gpu({**inp, **few})
-    assert torch.equal(o_all[:, :4], o_few), "O differs between the 8-wave and 4-wave forms"
-    assert torch.equal(l_all[:, :4], l_few), "LSE differs between the 8-wave and 4-wave forms"
+    o_296, l_296 = run_gpu(sub(296))
+    o_few, l_few = run_gpu(sub(4))
+    o_8, l_8 = run_gpu(sub(8))
+    assert torch.equal(o_all[:, :296], o_296) and torch.equal(l_all[:, :296], l_296), \
+        "256-row form: result depends on the grid"
+    assert torch.equal(o_8[:, :4], o_few) and torch.equal(l_8[:, :4], l_few), \
+        "two-key-group form: result depends on the grid"
+    few = sub(4)
+    O_ref, L_ref = attention_fp64(few["q"], few["k"], few["v"], inp["scale"], causal)
+    compare(o_all[:, :4], l_all[:, :4], O_ref, L_ref, dtype, "geometry 256-row form", src=few)
+    compare(o_few, l_few, O_ref, L_ref, dtype, "geometry two-key-group form", src=few)
+    if causal:  # row 0 sees key 0 alone in either form: O equals v_0 exactly
+        assert torch.equal(o_few[:, :, 0].cpu(), few["v"][:, :, 0])
+        assert torch.equal(o_all[:, :4, 0].cpu(), few["v"][:, :, 0])
 
 
 # ------------------------------------------------------------------------------------------

@@ -39,10 +39,11 @@ def note(msg: str):
     print(msg, flush=True)
 
 
-def run_bwd(inp, do, causal, scale=None):
+def run_bwd(inp, do, causal, scale=None, fwd=None):
+    """Gradients through fa_bwd; ``fwd``: (o, lse) to use instead of running fa_fwd here."""
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     dod = do.to(DEV)
-    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale) if fwd is None else (x.to(DEV) for x in fwd)
     dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
     fa.fa_bwd(q, k, v, o, dod, lse, dq, dk, dv, causal=causal, scale=scale)
     torch.cuda.synchronize()
@@ -167,16 +168,20 @@ def test_bwd_workload_sampled(name):
 @pytest.mark.parametrize("D,dtype,causal", [(64, "fp16", True), (128, "bf16", False)])
 def test_bwd_wide_grid_and_geometry(D, dtype, causal):
     # 300 heads of 300 rows: 600 dQ workgroups (ragged tails), checked on three heads against the oracle;
-    # the first 4 heads alone (a grid smaller than the CU count) must give bit-identical gradients
+    # the first 4 heads alone (a grid smaller than the CU count), given the same forward outputs, must
+    # give bit-identical gradients (the forward itself runs another form for 4 heads)
     inp = ai.make_custom(1, 300, 300, 300, D, dtype, causal, seed=95_000 + D)
     do = ai.make_dout((1, 300, 300, D), dtype, seed=95_100 + D)
     note(f"bwd wide B1 H300 300x300 D{D} {dtype} causal={causal}")
-    got = run_bwd(inp, do, causal)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd(q, k, v, causal=causal)
+    got = run_bwd(inp, do, causal, fwd=(o, lse))
     heads = [(0, 0), (0, 150), (0, 299)]
     ref = attention_bwd_fp64(inp["q"], inp["k"], inp["v"], do, inp["scale"], causal, heads=heads)
     compare(got, ref, dtype, "bwd wide", heads=heads)
     few = {n: inp[n][:, :4].contiguous() for n in ("q", "k", "v")}
-    got4 = run_bwd({**inp, **few}, do[:, :4].contiguous(), causal)
+    got4 = run_bwd({**inp, **few}, do[:, :4].contiguous(), causal,
+                   fwd=(o[:, :4].contiguous(), lse[:, :4].contiguous()))
     for name, x, y in zip(("dq", "dk", "dv"), got, got4):
         assert torch.equal(x[:, :4], y), f"{name} of the first 4 heads depends on the grid"
 

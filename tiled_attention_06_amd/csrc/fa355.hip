@@ -44,10 +44,10 @@ int launch_status() {
   return FA_ERR_LAUNCH;
 }
 
-template <int D, int DT, bool CAUSAL, bool DROP, int NW>
+template <int D, int DT, bool CAUSAL, bool DROP, int KG>
 int launch(const fa355::FwdParams& p, const fa355::MergeParams& m, hipStream_t stream) {
-  using G = fa355::Geo<D, NW>;
-  hipLaunchKernelGGL((fa355::fa_fwd_kernel<D, DT, CAUSAL, DROP, NW>), dim3(p.num_wg), dim3(G::NT), 0, stream, p);
+  using G = fa355::Geo<D, 8, KG>;
+  hipLaunchKernelGGL((fa355::fa_fwd_kernel<D, DT, CAUSAL, DROP, 8, KG>), dim3(p.num_wg), dim3(G::NT), 0, stream, p);
   int st = launch_status();
   if (st != FA_OK || p.n_split == 1) return st;
   constexpr int rows_per_block = 256 / (D / 4);
@@ -66,12 +66,12 @@ int launch(const fa355::FwdParams& p, const fa355::MergeParams& m, hipStream_t s
   return launch_status();
 }
 
-template <int D, bool DROP, int NW = 8>
+template <int D, bool DROP, int KG = 1>
 int dispatch_dtype(const fa355::FwdParams& p, const fa355::MergeParams& m, int dtype, bool causal, hipStream_t s) {
   if (dtype == FA_DTYPE_BF16)
-    return causal ? launch<D, fa355::DT_BF16, true, DROP, NW>(p, m, s)
-                  : launch<D, fa355::DT_BF16, false, DROP, NW>(p, m, s);
-  return causal ? launch<D, fa355::DT_F16, true, DROP, NW>(p, m, s) : launch<D, fa355::DT_F16, false, DROP, NW>(p, m, s);
+    return causal ? launch<D, fa355::DT_BF16, true, DROP, KG>(p, m, s)
+                  : launch<D, fa355::DT_BF16, false, DROP, KG>(p, m, s);
+  return causal ? launch<D, fa355::DT_F16, true, DROP, KG>(p, m, s) : launch<D, fa355::DT_F16, false, DROP, KG>(p, m, s);
 }
 
 // Compute units of the current device (0 if it cannot be read), cached per thread and device.
@@ -173,12 +173,12 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     if (st[i][2] > ((1ll << 31) - 1 - D) / (lens[i] + 256)) return FA_ERR_SHAPE;
   if (splits > 1 && ((int64_t)Lq + 256) * D * 4 >= (1ll << 32)) return FA_ERR_SHAPE;  // one partial slab
   // Workgroups of 8 waves and 256 rows; a single pass (no key splits) whose grid
-  // would not exceed the CU count takes 4 waves and 128 rows instead:
-  // twice the workgroups, and the heaviest causal ones half as long (measured on
-  // the 1x32x2048x128 causal shape: 59.4 -> 51.6 us; on larger grids the
-  // 8-wave form is faster).
+  // would not exceed the CU count takes 128 rows per workgroup instead, with the
+  // 8 waves in two key groups that take alternate key tiles: twice the
+  // workgroups, the heaviest causal ones half as long, and still two waves per
+  // SIMD.
   const int BR8 = fa355::Geo<128>::BR;
-  static_assert(fa355::Geo<64>::BR == fa355::Geo<128>::BR && fa355::Geo<64, 4>::BR == fa355::Geo<128, 4>::BR,
+  static_assert(fa355::Geo<64>::BR == fa355::Geo<128>::BR && fa355::Geo<64, 8, 2>::BR == fa355::Geo<128, 8, 2>::BR,
                 "row tile independent of D");
   int64_t n_qt = ((int64_t)Lq + BR8 - 1) / BR8;
   bool narrow = false;
@@ -186,7 +186,7 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const int cus = cu_count();
     narrow = cus > 0 && (int64_t)B * H * n_qt <= cus;
   }
-  if (narrow) n_qt = ((int64_t)Lq + fa355::Geo<128, 4>::BR - 1) / fa355::Geo<128, 4>::BR;
+  if (narrow) n_qt = ((int64_t)Lq + fa355::Geo<128, 8, 2>::BR - 1) / fa355::Geo<128, 8, 2>::BR;
   const int64_t num_wg = (int64_t)B * H * n_qt * splits;
   if ((int64_t)B * H >= (1ll << 31) || num_wg >= (1ll << 22)) return FA_ERR_SHAPE;
 
@@ -242,14 +242,14 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (drop_t < 256) {  // (only the single-pass entry point takes a dropout probability)
     if (narrow)
-      return D == 128 ? dispatch_dtype<128, true, 4>(p, m, dtype, causal != 0, s)
-                      : dispatch_dtype<64, true, 4>(p, m, dtype, causal != 0, s);
+      return D == 128 ? dispatch_dtype<128, true, 2>(p, m, dtype, causal != 0, s)
+                      : dispatch_dtype<64, true, 2>(p, m, dtype, causal != 0, s);
     return D == 128 ? dispatch_dtype<128, true>(p, m, dtype, causal != 0, s)
                     : dispatch_dtype<64, true>(p, m, dtype, causal != 0, s);
   }
   if (narrow)
-    return D == 128 ? dispatch_dtype<128, false, 4>(p, m, dtype, causal != 0, s)
-                    : dispatch_dtype<64, false, 4>(p, m, dtype, causal != 0, s);
+    return D == 128 ? dispatch_dtype<128, false, 2>(p, m, dtype, causal != 0, s)
+                    : dispatch_dtype<64, false, 2>(p, m, dtype, causal != 0, s);
   return D == 128 ? dispatch_dtype<128, false>(p, m, dtype, causal != 0, s)
                   : dispatch_dtype<64, false>(p, m, dtype, causal != 0, s);
 }

@@ -7,8 +7,9 @@
 //
 // One workgroup = 8 waves (two per SIMD) = 256 query rows of one (batch, head);
 // each wave owns 32 rows.  One workgroup per CU.  (Grids with no more such
-// workgroups than CUs use 4 waves and 128 rows instead: twice the workgroups,
-// one wave per SIMD.)  The method ([DF §2.2], first
+// workgroups than CUs use 128 rows per workgroup instead: twice the workgroups,
+// and waves w and w+4 own the same rows and take alternate key tiles, merging
+// their partial results through LDS at the end.)  The method ([DF §2.2], first
 // and second layers; [OP §2.1], a loop over key blocks inside a loop over query
 // blocks):
 //   * the Q tile is loaded once and stays in VGPRs as MFMA operands;
@@ -308,14 +309,17 @@ __device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Tile geometry shared by the kernel and the host launcher.  NW_ = 8: two waves
-// per SIMD, 256 query rows per workgroup (the default); NW_ = 4: one wave per
-// SIMD and 128 rows, for grids too small to give every CU a workgroup otherwise.
-template <int D, int NW_ = 8>
+// Tile geometry shared by the kernel and the host launcher: NW_ = 8 waves, two
+// per SIMD.  KG_ = 1: 256 query rows per workgroup, every wave takes every key
+// tile (the default).  KG_ = 2: 128 rows, and the waves form two key groups of
+// four that share those rows and take alternate key tiles, for grids too small
+// to give every CU a workgroup of 256 rows.
+template <int D, int NW_ = 8, int KG_ = 1>
 struct Geo {
   static constexpr int NW = NW_;               // waves per workgroup
+  static constexpr int KG = KG_;               // key groups
   static constexpr int NT = 64 * NW;           // threads per workgroup
-  static constexpr int BR = 32 * NW;           // query rows per workgroup
+  static constexpr int BR = 32 * NW / KG;      // query rows per workgroup
   static constexpr int BC = 64;                // keys per K/V tile
   static constexpr int KB = BC / 32;           // 32-key blocks of a tile (Sᵀ MFMA row blocks)
   static constexpr int NB = D / 32;            // 32-dim blocks of the output (Oᵀ MFMA row blocks)
@@ -335,11 +339,12 @@ struct Geo {
   static constexpr int LDS = NS * (KT + VT);
   static_assert(NBLK % NW == 0 && 32 % NBLK == 0 && NBLK >= 8, "copy and read layout");
   static_assert(LDS <= 163840, "one workgroup per CU");
+  static_assert(KG == 1 || (KG == 2 && NW == 8), "key groups of four waves");
 };
 
-template <int D, int DT, bool CAUSAL, bool DROP, int NW = 8>
+template <int D, int DT, bool CAUSAL, bool DROP, int NW = 8, int KG = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(FwdParams p) {
-  using G = Geo<D, NW>;
+  using G = Geo<D, NW, KG>;
   constexpr int BC = G::BC, KB = G::KB, NB = G::NB, KS = G::KS, NCH = G::NCH;
   constexpr int NBLK = G::NBLK, KBS = G::KBS, VBS = G::VBS, KT = G::KT, VT = G::VT;
   constexpr float NEG_INF = -__builtin_inff();
@@ -394,7 +399,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   qt_r = __builtin_amdgcn_readfirstlane(qt_r);
   const int qt = CAUSAL ? p.n_qt - 1 - qt_r : qt_r;
   const int i0 = qt * G::BR;
-  const int i0w = i0 + 32 * wave;
+  // rows of this wave; with two key groups, waves w and w + NW/2 share rows
+  const int wr = KG == 2 ? wave & (NW / 2 - 1) : wave;
+  const int kg = KG == 2 ? wave / (NW / 2) : 0;  // key group (wave-uniform)
+  const int i0w = i0 + 32 * wr;
   const int Lq = p.Lq, Lk = p.Lk;
 
   // (batch, head) slabs; a slab's rows are q_sl (k_sl, ...) elements apart and its
@@ -467,8 +475,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const u32x4 x = buf_load16(qrs, (uint32_t)(qrow * q_sl + 16 * s + 8 * g) * 2);
     qr[s] = (x & p.q_and) ^ p.q_xor;
   }
-  // K and V tiles 0..NS-2, in the order the loop continues: K t, V t per tile.
-  // stage of tile t: (t - t_b) % NS
+  // stage of tile t: (t - t_b) % NS.  One key group: K and V of tiles t_b ..
+  // t_b+2, in the order the loop continues (K t, V t per tile).  Two key groups:
+  // K of tiles t_b .. t_b+3 and V of tiles t_b, t_b+1.
   if (t_b < t_e) {
     copy_k(t_b, I0{});
     copy_v(t_b, I0{});
@@ -479,8 +488,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   if (t_b + 2 < t_e) {
     copy_k(t_b + 2, std::integral_constant<int, 2>{});
-    copy_v(t_b + 2, std::integral_constant<int, 2>{});
+    if constexpr (KG == 1) copy_v(t_b + 2, std::integral_constant<int, 2>{});
   }
+  if constexpr (KG == 2)
+    if (t_b + 3 < t_e) copy_k(t_b + 3, std::integral_constant<int, 3>{});
 
   // per-lane LDS offsets of the MFMA operand reads.  Tile row r sits in block
   // r % NBLK at position r / NBLK; rows r and r + 8m (m >= 0, r < 8) differ by a
@@ -516,10 +527,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   n_full = min(n_full, t_e);
 
   // mask of a tile crossing the diagonal or the end of the keys (wave-uniform test)
+  auto need_mask = [&](int t) { return (CAUSAL && t * BC + BC - 1 > i0w + off) || (t * BC + BC > Lk); };
   auto mask_tile = [&](f32x16(&S)[KB], int t) {
     const int j0 = t * BC;
-    const bool need_mask = (CAUSAL && j0 + BC - 1 > i0w + off) || (j0 + BC > Lk);
-    if (need_mask) {
+    if (need_mask(t)) {
       // key offset within the tile of S[kb][r] is 32kb + 8(r/4) + 4g + r%4
       // (lane-derived values taken afresh, see opaque())
       const int lane_m = opaque(tid) & 63;
@@ -664,84 +675,191 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
   auto end_iter = [&](int) { wait_join(); };
 
-  wait_join();  // the first three tiles and Q are in
-  f32x16 sA[KB], sB[KB];
-  float mxA = NEG_INF, mxB = NEG_INF;
-  int t_tail = t_b;
-  if (n_full > t_b) {
-    // ---- full tiles, software-pipelined: iteration t computes Sᵀ of tile t+1
-    // and its row max while the weights and PV of tile t run; the rescale for
-    // tile t uses the max found one iteration earlier.  No mask and no branch
-    // inside the body (a wave with no live rows skips it whole).
-    if (live) {
-      compute_s(kst(I0{}), sA);
+  auto copy_k_rt = [&](int t) {
+    switch ((t - t_b) & 3) {
+      case 0: copy_k(t, I0{}); break;
+      case 1: copy_k(t, std::integral_constant<int, 1>{}); break;
+      case 2: copy_k(t, std::integral_constant<int, 2>{}); break;
+      default: copy_k(t, std::integral_constant<int, 3>{}); break;
+    }
+  };
+  auto copy_v_rt = [&](int t) {
+    switch ((t - t_b) & 3) {
+      case 0: copy_v(t, I0{}); break;
+      case 1: copy_v(t, std::integral_constant<int, 1>{}); break;
+      case 2: copy_v(t, std::integral_constant<int, 2>{}); break;
+      default: copy_v(t, std::integral_constant<int, 3>{}); break;
+    }
+  };
+  if constexpr (KG == 1) {
+    wait_join();  // the first three tiles and Q are in
+    f32x16 sA[KB], sB[KB];
+    float mxA = NEG_INF, mxB = NEG_INF;
+    int t_tail = t_b;
+    if (n_full > t_b) {
+      // ---- full tiles, software-pipelined: iteration t computes Sᵀ of tile t+1
+      // and its row max while the weights and PV of tile t run; the rescale for
+      // tile t uses the max found one iteration earlier.  No mask and no branch
+      // inside the body (a wave with no live rows skips it whole).
+      if (live) {
+        compute_s(kst(I0{}), sA);
+        mxA = row_max(sA);
+      }
+      auto it_main = [&](int t, f32x16(&Sc)[KB], f32x16(&Sn)[KB], float& mxc, float& mxn, auto Pc) {
+        constexpr int P = decltype(Pc)::value;
+        using PN = std::integral_constant<int, (P + 1) % G::NS>;
+        using PC = std::integral_constant<int, (P + G::NS - 1) % G::NS>;
+        if (live) rescale(mxc);
+        if (t + G::NS - 1 < t_e) {
+          copy_k(t + G::NS - 1, PC{});
+          copy_v(t + G::NS - 1, PC{});
+        }
+        if (live) {
+          // LLVM's interleave strategy for small-GEMM bodies (MFMAs spaced between the
+          // LDS operand reads and the VALU work): 1.8% faster on the 7B 4K shape than
+          // the default schedule, same results
+          __builtin_amdgcn_iglp_opt(0);
+          compute_s(kst(PN{}), Sn);
+          u32x4 pb[KB][2];
+          make_p(Sc, pb, t, std::true_type{});
+          pv(pb, vst(Pc));
+          mxn = row_max(Sn);
+        }
+        end_iter(t);
+      };
+      static_assert(G::NS == 4, "the loop below is unrolled over the stages");
+      for (int t = t_b; t + 1 < n_full; t += 4) {
+        it_main(t, sA, sB, mxA, mxB, I0{});
+        if (t + 2 < n_full) it_main(t + 1, sB, sA, mxB, mxA, std::integral_constant<int, 1>{});
+        if (t + 3 < n_full) it_main(t + 2, sA, sB, mxA, mxB, std::integral_constant<int, 2>{});
+        if (t + 4 < n_full) it_main(t + 3, sB, sA, mxB, mxA, std::integral_constant<int, 3>{});
+      }
+      // weights and PV of the last full tile, whose Sᵀ is already computed
+      const int tf = n_full - 1;
+      auto finish = [&](f32x16(&Sc)[KB], float mxc) {
+        if (live) rescale(mxc);
+        if (tf + G::NS - 1 < t_e) copies_rt(tf);
+        if (live) {
+          u32x4 pb[KB][2];
+          make_p(Sc, pb, tf, std::false_type{});
+          pv(pb, vst_rt((tf - t_b) % G::NS));
+        }
+        end_iter(tf);
+      };
+      if ((tf - t_b) & 1)
+        finish(sB, mxB);
+      else
+        finish(sA, mxA);
+      t_tail = n_full;
+    }
+    // ---- tiles that cross the diagonal or the end of the keys: not pipelined,
+    // masked; a wave skips tiles above its own rows but still copies and joins.
+    for (int t = t_tail; t < t_e; ++t) {
+      if (t + G::NS - 1 < t_e) copies_rt(t);
+      if (live && active(t)) {
+        compute_s(kst_rt((t - t_b) % G::NS), sA);
+        // (scheduling barriers: the operand reads of one product are not hoisted
+        // over the softmax, which would run this path out of registers)
+        __builtin_amdgcn_sched_barrier(0);
+        mask_tile(sA, t);
+        const bool any = move_max(row_max(sA));
+        u32x4 pb[KB][2];
+        make_p(sA, pb, t, std::false_type{});
+        scale_o(any);
+        __builtin_amdgcn_sched_barrier(0);
+        pv(pb, vst_rt((t - t_b) % G::NS));
+      }
+      end_iter(t);
+    }
+
+  } else {
+    // ---- two key groups: group kg takes tiles t_b+kg, t_b+kg+2, ...; step s covers
+    // tiles t_b+2s and t_b+2s+1.  Each group runs the software pipeline of the
+    // one-group loop over its own tiles: Sᵀ of its next tile while the weights and
+    // PV of the current one run.  A tile that crosses the diagonal or the end of the
+    // keys is masked at the start of its step and its max taken again.  Step s
+    // copies K of tiles t_b+2s+4 and +5 into the stages of the step's own tiles
+    // (whose Sᵀ was made one step earlier) and V of tiles t_b+2s+2 and +3 into the
+    // stages of the previous step's tiles (whose PV ran one step earlier).
+    wait_join();  // the first tiles and Q are in
+    f32x16 sA[KB], sB[KB];
+    float mxA = NEG_INF, mxB = NEG_INF;
+    const int t0 = t_b + kg;
+    if (live && t0 < t_e && active(t0)) {
+      compute_s(kst_rt((t0 - t_b) & 3), sA);
       mxA = row_max(sA);
     }
-    auto it_main = [&](int t, f32x16(&Sc)[KB], f32x16(&Sn)[KB], float& mxc, float& mxn, auto Pc) {
-      constexpr int P = decltype(Pc)::value;
-      using PN = std::integral_constant<int, (P + 1) % G::NS>;
-      using PC = std::integral_constant<int, (P + G::NS - 1) % G::NS>;
-      if (live) rescale(mxc);
-      if (t + G::NS - 1 < t_e) {
-        copy_k(t + G::NS - 1, PC{});
-        copy_v(t + G::NS - 1, PC{});
-      }
-      if (live) {
-        // LLVM's interleave strategy for small-GEMM bodies (MFMAs spaced between the
-        // LDS operand reads and the VALU work): 1.8% faster on the 7B 4K shape than
-        // the default schedule, same results
+    wait_join();  // every wave is done with the K stages that step 0 refills
+    const int n_steps = (t_e - t_b + 1) >> 1;
+    auto kstep = [&](int s, f32x16(&Sc)[KB], f32x16(&Sn)[KB], float& mxc, float& mxn) {
+      const int tc = t_b + 2 * s;
+      if (tc + 4 < t_e) copy_k_rt(tc + 4);
+      if (tc + 5 < t_e) copy_k_rt(tc + 5);
+      if (tc + 2 < t_e) copy_v_rt(tc + 2);
+      if (tc + 3 < t_e) copy_v_rt(tc + 3);
+      const int t = tc + kg;
+      if (live && t < t_e && active(t)) {
+        if (need_mask(t)) {
+          mask_tile(Sc, t);
+          mxc = row_max(Sc);
+        }
+        rescale(mxc);
+        // LLVM's interleave strategy for small-GEMM bodies, as in the one-group loop.
+        // Sᵀ of the group's next tile is made even when that tile lies past the end
+        // or above the wave's rows (then from a stage no copy is writing in this
+        // step, and never used): one straight block per step.  (Peeling the last
+        // step to skip it costs more in spills than the products it saves.)
         __builtin_amdgcn_iglp_opt(0);
-        compute_s(kst(PN{}), Sn);
+        compute_s(kst_rt((t + 2 - t_b) & 3), Sn);
         u32x4 pb[KB][2];
         make_p(Sc, pb, t, std::true_type{});
-        pv(pb, vst(Pc));
+        pv(pb, vst_rt((t - t_b) & 3));
         mxn = row_max(Sn);
       }
       end_iter(t);
     };
-    static_assert(G::NS == 4, "the loop below is unrolled over the stages");
-    for (int t = t_b; t + 1 < n_full; t += 4) {
-      it_main(t, sA, sB, mxA, mxB, I0{});
-      if (t + 2 < n_full) it_main(t + 1, sB, sA, mxB, mxA, std::integral_constant<int, 1>{});
-      if (t + 3 < n_full) it_main(t + 2, sA, sB, mxA, mxB, std::integral_constant<int, 2>{});
-      if (t + 4 < n_full) it_main(t + 3, sB, sA, mxB, mxA, std::integral_constant<int, 3>{});
+    for (int s = 0; s < n_steps; s += 2) {
+      kstep(s, sA, sB, mxA, mxB);
+      if (s + 1 < n_steps) kstep(s + 1, sB, sA, mxB, mxA);
     }
-    // weights and PV of the last full tile, whose Sᵀ is already computed
-    const int tf = n_full - 1;
-    auto finish = [&](f32x16(&Sc)[KB], float mxc) {
-      if (live) rescale(mxc);
-      if (tf + G::NS - 1 < t_e) copies_rt(tf);
-      if (live) {
-        u32x4 pb[KB][2];
-        make_p(Sc, pb, tf, std::false_type{});
-        pv(pb, vst_rt((tf - t_b) % G::NS));
-      }
-      end_iter(tf);
-    };
-    if ((tf - t_b) & 1)
-      finish(sB, mxB);
-    else
-      finish(sA, mxA);
-    t_tail = n_full;
-  }
-  // ---- tiles that cross the diagonal or the end of the keys: not pipelined,
-  // masked; a wave skips tiles above its own rows but still copies and joins.
-  for (int t = t_tail; t < t_e; ++t) {
-    if (t + G::NS - 1 < t_e) copies_rt(t);
-    if (live && active(t)) {
-      compute_s(kst_rt((t - t_b) % G::NS), sA);
-      // (scheduling barriers: the operand reads of one product are not hoisted
-      // over the softmax, which would run this path out of registers)
-      __builtin_amdgcn_sched_barrier(0);
-      mask_tile(sA, t);
-      const bool any = move_max(row_max(sA));
-      u32x4 pb[KB][2];
-      make_p(sA, pb, t, std::false_type{});
-      scale_o(any);
-      __builtin_amdgcn_sched_barrier(0);
-      pv(pb, vst_rt((t - t_b) % G::NS));
+    // The two groups' partial results for the same rows meet in LDS (every copy has
+    // landed and every read of the ring finished before the last barrier): group 1
+    // leaves its output accumulators in V stage wr and its running max and sums in
+    // xst; group 0 combines them with its own (the running maxima and exp-sums of
+    // disjoint key sets combine exactly, as across key splits) and goes on to the
+    // epilogue.
+    __shared__ float xst[NW / 2][3][64];
+    float* const xo = (float*)vst_rt(wr);
+    static_assert(NB * 16 * 64 * 4 <= VT, "one wave's accumulators fit a V stage");
+    if (kg == 1 && live) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(f32x4*)(xo + ((nb * 4 + q4) * 64 + lane) * 4) =
+              f32x4{oacc[nb][4 * q4], oacc[nb][4 * q4 + 1], oacc[nb][4 * q4 + 2], oacc[nb][4 * q4 + 3]};
+      xst[wr][0][lane] = m_run;
+      xst[wr][1][lane] = l_f;
+      xst[wr][2][lane] = l_r;
     }
-    end_iter(t);
+    __syncthreads();
+    if (kg == 1) return;
+    if (live) {
+      const float m1 = xst[wr][0][lane];
+      const float mm = fmaxf(m_run, m1);
+      const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 x = *(const f32x4*)(xo + ((nb * 4 + q4) * 64 + lane) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[nb][4 * q4 + i] = oacc[nb][4 * q4 + i] * a0 + x[i] * a1;
+        }
+      l_f = l_f * a0 + xst[wr][1][lane] * a1;
+      l_r = l_r * a0 + xst[wr][2][lane] * a1;
+      m_run = mm;
+    }
   }
 
   // ---- epilogue.  The lane's row and half are derived afresh (see opaque()).
