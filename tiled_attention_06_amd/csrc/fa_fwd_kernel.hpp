@@ -888,8 +888,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     return;
   }
-  // one pass: normalise by the sum of the rounded weights, store O and LSE
+  // one pass: normalise by the sum of the rounded weights, store O and LSE.  The
+  // accumulator layout gives a lane 4 dims of one row per 8 bytes, scattered over
+  // 32 rows per instruction; the wave first lays its 32 rows out row-major in an
+  // LDS stage of the ring (free since the last barrier: every copy has landed and
+  // every read is done; one stage per wave, and with two key groups only group 0,
+  // waves 0..3, gets here, after group 1's hand-over through the V stages), then
+  // stores whole rows, 16 bytes per lane.  Rows are OPITCH bytes apart in LDS
+  // (16 bytes of pad: 16-byte aligned row reads, and the 8-byte writes of lanes
+  // 0..15 on distinct banks).
   const float inv = DROP ? p.drop_scale / lr_t : 1.0f / lr_t;
+  constexpr int OPITCH = 2 * D + 16;
+  static_assert(32 * OPITCH <= KT && 32 * OPITCH <= VT, "one wave's output rows fit a stage");
+  unsigned char* const stg = wave < 4 ? kst_rt(wave) : vst_rt(wave - 4);
+  const int l32_e = lane_e & 31;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -897,8 +909,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int d0 = 32 * nb + 8 * q4 + 4 * g_e;
       const u32x2 w = {pack2<DT>(oacc[nb][4 * q4] * inv, oacc[nb][4 * q4 + 1] * inv),
                        pack2<DT>(oacc[nb][4 * q4 + 2] * inv, oacc[nb][4 * q4 + 3] * inv)};
-      buf_store8(ors, (uint32_t)(row_e * o_sl + d0) * 2, w);  // rows >= Lq are dropped
+      *(u32x2*)(stg + l32_e * OPITCH + d0 * 2) = w;
     }
+  // (the wave reads back only what its own lanes wrote, and LDS keeps one wave's
+  // accesses in order: no barrier)
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int j = 0; j < 32 * CPR / 64; ++j) {
+    const int r = j * (64 / CPR) + lane_e / CPR, ch = lane_e % CPR;
+    const u32x4 x = *(const u32x4*)(stg + r * OPITCH + ch * 16);
+    buf_store16(ors, (uint32_t)((i0w + r) * o_sl + ch * 8) * 2, x);  // rows >= Lq are dropped
+  }
   if (g_e == 0 && row_e < Lq) p.lse[(size_t)bh * Lq + row_e] = (m_run + log2f(lf_t)) * 0.69314718055994530942f;
 }
 
