@@ -334,7 +334,7 @@ struct Geo {
   static constexpr int KBS = 1024 + 16;        // bytes per K block (rows 16 bytes apart in bank space)
   static constexpr int VBS = 1024 + 64;        // bytes per V block (rows 64 bytes apart in bank space)
   static constexpr int KT = NBLK * KBS, VT = NBLK * VBS;  // bytes per K / V tile
-  static constexpr int CPW = NBLK / NW;        // copy instructions per wave and tile
+
   static constexpr int NS = 4;                 // K and V tiles resident in LDS (ring of stages)
   static constexpr int LDS = NS * (KT + VT);
   static_assert(NBLK % NW == 0 && 32 % NBLK == 0 && NBLK >= 8, "copy and read layout");
@@ -347,6 +347,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   using G = Geo<D, NW, KG>;
   constexpr int BC = G::BC, KB = G::KB, NB = G::NB, KS = G::KS, NCH = G::NCH;
   constexpr int NBLK = G::NBLK, KBS = G::KBS, VBS = G::VBS, KT = G::KT, VT = G::VT;
+  // Tile copies are issued by waves 0..NWC-1: without dropout one wave per SIMD
+  // (waves w and w+4 share a SIMD).  The copy instructions of a step are slow to
+  // issue when all waves issue them at once after the barrier; this way the
+  // other wave of each SIMD goes straight on with its products (1-2% faster).
+  // The dropout kernels keep every wave copying: they are register-bound, and
+  // the longer copy sequence made them spill.
+  constexpr int NWC = DROP ? NW : 4;
+  constexpr int CPW = NBLK / NWC;  // copy instructions per copying wave and tile
+  static_assert(NBLK % NWC == 0 && NW >= NWC && 3 * CPW <= 15, "copy layout, vmcnt immediates");
   constexpr float NEG_INF = -__builtin_inff();
   // One array per stage: the compiler can then tell that a tile copy in flight
   // into one stage does not alias reads of another, and waits for it only where
@@ -416,7 +425,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const auto qrs = make_rsrc(qslab, (uint32_t)((Lq - 1) * q_sl + D) * 2);
   const auto ors = make_rsrc(oslab, (uint32_t)((Lq - 1) * o_sl + D) * 2);
 
-  // ---- HBM -> LDS copy of one tile.  Copy j of wave w fills block b = w + NW·j:
+  // ---- HBM -> LDS copy of one tile.  Copy j of wave w < NWC fills block b = w + NWC·j:
   // lane l brings the 16-byte chunk l % NCH of tile row b + NBLK·(l / NCH).  The
   // buffer resource starts at the tile's first key and ends with the last key's
   // row, so keys >= Lk read 0; the per-lane offset is the same for every tile.
@@ -426,10 +435,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // its last row, and the offset between a wave's copies
   const int64_t tb_k = (int64_t)BC * k_sl * 2, tb_v = (int64_t)BC * v_sl * 2;
   const uint32_t end_k = (uint32_t)((Lk - 1) * k_sl + D) * 2, end_v = (uint32_t)((Lk - 1) * v_sl + D) * 2;
-  const uint32_t step_k = (uint32_t)(G::NW * k_sl * 2), step_v = (uint32_t)(G::NW * v_sl * 2);
+  const uint32_t step_k = (uint32_t)(NWC * k_sl * 2), step_v = (uint32_t)(NWC * v_sl * 2);
   auto copy_tile = [&](const char* slab, int64_t tb, uint32_t end, uint32_t step, uint32_t lane_src,
                        unsigned char* dst, int tile, auto BSc) {
     constexpr int BS = decltype(BSc)::value;
+    if constexpr (NWC < NW)
+      if (wave >= NWC) return;  // wave-uniform
     const int64_t off = (int64_t)tile * tb;
     const uint64_t base = (uint64_t)(uintptr_t)(slab + off);
     const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
@@ -437,11 +448,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(end - (uint32_t)off)),
                       (uint32_t)kBufferFlags};
     const uint32_t l0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_addr(dst) + BS * wave));
-    if constexpr (G::CPW == 2)
-      dma16x2(rs, l0, lane_src, l0 + BS * G::NW, lane_src + step);
-    else
 #pragma unroll
-      for (int j = 0; j < G::CPW; ++j) dma16(rs, l0 + BS * G::NW * j, lane_src + step * j);
+    for (int j = 0; j < CPW; j += 2) {
+      if (j + 1 < CPW)
+        dma16x2(rs, l0 + BS * NWC * j, lane_src + step * j, l0 + BS * NWC * (j + 1), lane_src + step * (j + 1));
+      else
+        dma16(rs, l0 + BS * NWC * j, lane_src + step * j);
+    }
+
   };
   auto copy_k = [&](int tile, auto Sc) {
     copy_tile(kslab, tb_k, end_k, step_k, src_k, kst(Sc), tile, std::integral_constant<int, KBS>{});
@@ -475,23 +489,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const u32x4 x = buf_load16(qrs, (uint32_t)(qrow * q_sl + 16 * s + 8 * g) * 2);
     qr[s] = (x & p.q_and) ^ p.q_xor;
   }
-  // stage of tile t: (t - t_b) % NS.  One key group: K and V of tiles t_b ..
-  // t_b+2, in the order the loop continues (K t, V t per tile).  Two key groups:
-  // K of tiles t_b .. t_b+3 and V of tiles t_b, t_b+1.
-  if (t_b < t_e) {
-    copy_k(t_b, I0{});
-    copy_v(t_b, I0{});
-  }
-  if (t_b + 1 < t_e) {
-    copy_k(t_b + 1, std::integral_constant<int, 1>{});
-    copy_v(t_b + 1, std::integral_constant<int, 1>{});
-  }
-  if (t_b + 2 < t_e) {
-    copy_k(t_b + 2, std::integral_constant<int, 2>{});
-    if constexpr (KG == 1) copy_v(t_b + 2, std::integral_constant<int, 2>{});
-  }
+  // stage of tile t: (t - t_b) % NS.  Only what the first Sᵀ needs is copied
+  // before the first wait (K of tile t_b, and with two key groups of t_b+1 too);
+  // the other first tiles follow once it is in, while that Sᵀ is computed.
+  if (t_b < t_e) copy_k(t_b, I0{});
   if constexpr (KG == 2)
-    if (t_b + 3 < t_e) copy_k(t_b + 3, std::integral_constant<int, 3>{});
+    if (t_b + 1 < t_e) copy_k(t_b + 1, std::integral_constant<int, 1>{});
 
   // per-lane LDS offsets of the MFMA operand reads.  Tile row r sits in block
   // r % NBLK at position r / NBLK; rows r and r + 8m (m >= 0, r < 8) differ by a
@@ -692,19 +695,43 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
   if constexpr (KG == 1) {
-    wait_join();  // the first three tiles and Q are in
+    wait_join();  // Q and K of tile t_b are in
+    // V of tile t_b, then K and V of tiles t_b+1 and t_b+2, in the order the loop
+    // needs them (the steps copy tile t+3 in step t)
+    if (t_b < t_e) copy_v(t_b, I0{});
+    if (t_b + 1 < t_e) {
+      copy_k(t_b + 1, std::integral_constant<int, 1>{});
+      copy_v(t_b + 1, std::integral_constant<int, 1>{});
+    }
+    if (t_b + 2 < t_e) {
+      copy_k(t_b + 2, std::integral_constant<int, 2>{});
+      copy_v(t_b + 2, std::integral_constant<int, 2>{});
+    }
     f32x16 sA[KB], sB[KB];
     float mxA = NEG_INF, mxB = NEG_INF;
+    // Sᵀ of the first full tile while those copies land
+    if (n_full > t_b && live) {
+      compute_s(kst(I0{}), sA);
+      mxA = row_max(sA);
+    }
+    // then wait only for V of tile t_b and K of tile t_b+1 (the copies return in
+    // the order they were issued: those of V(t_b+1), K(t_b+2), V(t_b+2) may still
+    // be in flight) and join
+    if (t_b + 2 < t_e)
+      __builtin_amdgcn_s_waitcnt(((3 * CPW) & 15) | (7 << 4) | (15 << 8));
+    else if (t_b + 1 < t_e)
+      __builtin_amdgcn_s_waitcnt((CPW & 15) | (7 << 4) | (15 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     int t_tail = t_b;
     if (n_full > t_b) {
       // ---- full tiles, software-pipelined: iteration t computes Sᵀ of tile t+1
       // and its row max while the weights and PV of tile t run; the rescale for
       // tile t uses the max found one iteration earlier.  No mask and no branch
       // inside the body (a wave with no live rows skips it whole).
-      if (live) {
-        compute_s(kst(I0{}), sA);
-        mxA = row_max(sA);
-      }
       auto it_main = [&](int t, f32x16(&Sc)[KB], f32x16(&Sn)[KB], float& mxc, float& mxn, auto Pc) {
         constexpr int P = decltype(Pc)::value;
         using PN = std::integral_constant<int, (P + 1) % G::NS>;
@@ -781,7 +808,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // copies K of tiles t_b+2s+4 and +5 into the stages of the step's own tiles
     // (whose Sᵀ was made one step earlier) and V of tiles t_b+2s+2 and +3 into the
     // stages of the previous step's tiles (whose PV ran one step earlier).
-    wait_join();  // the first tiles and Q are in
+    wait_join();  // Q and K of tiles t_b, t_b+1 are in
+    // V of tiles t_b, t_b+1 and K of tiles t_b+2, t_b+3 while the first Sᵀ is made
+    if (t_b < t_e) copy_v(t_b, I0{});
+    if (t_b + 1 < t_e) copy_v(t_b + 1, std::integral_constant<int, 1>{});
+    if (t_b + 2 < t_e) copy_k(t_b + 2, std::integral_constant<int, 2>{});
+    if (t_b + 3 < t_e) copy_k(t_b + 3, std::integral_constant<int, 3>{});
     f32x16 sA[KB], sB[KB];
     float mxA = NEG_INF, mxB = NEG_INF;
     const int t0 = t_b + kg;
@@ -789,7 +821,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       compute_s(kst_rt((t0 - t_b) & 3), sA);
       mxA = row_max(sA);
     }
-    wait_join();  // every wave is done with the K stages that step 0 refills
+    wait_join();  // those copies are in, and every wave is done with the K stages that step 0 refills
     const int n_steps = (t_e - t_b + 1) >> 1;
     auto kstep = [&](int s, f32x16(&Sc)[KB], f32x16(&Sn)[KB], float& mxc, float& mxn) {
       const int tc = t_b + 2 * s;
