@@ -99,18 +99,47 @@ __device__ __forceinline__ float2 unpack2(uint32_t u) {
 // Tile copies HBM -> LDS for the backward kernels: a tile of 64 rows of one
 // (batch, head) slab into the forward pass's row image (block pitch KBS) or
 // transposing image (block pitch VBS).  Copy j of wave w fills block w + NW·j.
-template <int D, int NW>
+// Store a wave's 32 rows (row r0 + l%32, dims 32nb + 8(r/4) + 4g + r%4 in lane l,
+// register r of acc[nb]) times sc, rounded to the input type: the rows are laid out
+// row-major in the LDS buffer stg (rows 2·D + 16 bytes apart: 16-byte aligned row
+// reads, the 8-byte writes of 16 lanes on distinct banks), then stored as whole
+// rows, 16 bytes per lane, instead of 8-byte pieces scattered over 32 rows per
+// instruction.  The wave reads back only what its own lanes wrote (LDS keeps a
+// wave's accesses in order).  Rows past the buffer range's end are dropped.
+template <int D, int DT>
+__device__ __forceinline__ void stage_rows_out(const f32x16 (&acc)[D / 32], float sc, unsigned char* stg, int lane,
+                                               __amdgpu_buffer_rsrc_t rs, int r0, int row_stride) {
+  constexpr int PITCH = 2 * D + 16, CPR = D / 8;
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * nb + 8 * q4 + 4 * g;
+      *(u32x2*)(stg + l32 * PITCH + d0 * 2) =
+          u32x2{pack2<DT>(acc[nb][4 * q4] * sc, acc[nb][4 * q4 + 1] * sc),
+                pack2<DT>(acc[nb][4 * q4 + 2] * sc, acc[nb][4 * q4 + 3] * sc)};
+    }
+#pragma unroll
+  for (int j = 0; j < 32 * CPR / 64; ++j) {
+    const int r = j * (64 / CPR) + lane / CPR, ch = lane % CPR;
+    buf_store16(rs, (uint32_t)((r0 + r) * row_stride + ch * 8) * 2, *(const u32x4*)(stg + r * PITCH + ch * 16));
+  }
+}
+
+template <int D, int NW, int NWC = NW>
 struct BwdCopy {
   using G = Geo<D>;
-  static constexpr int NCH = G::NCH, NBLK = G::NBLK, CPW = NBLK / NW;
-  static_assert(NBLK % NW == 0, "copy layout");
+  // waves 0..NWC-1 issue the copies, CPW each per tile
+  static constexpr int NCH = G::NCH, NBLK = G::NBLK, CPW = NBLK / NWC;
+  static_assert(NBLK % NWC == 0 && NWC <= NW, "copy layout");
   uint32_t lane_src, step, row_bytes;  // per-lane source offset in a tile, offset between a wave's copies
   int wave;
   __device__ __forceinline__ BwdCopy(int wave_, int lane, int row_stride) : wave(wave_) {
     row_bytes = (uint32_t)row_stride * 2u;
     const int lrow = wave_ + NBLK * (lane / NCH), lchunk = 16 * (lane % NCH);
     lane_src = (uint32_t)lrow * row_bytes + (uint32_t)lchunk;
-    step = (uint32_t)NW * row_bytes;
+    step = (uint32_t)NWC * row_bytes;
   }
   // rows [64·tile, 64·tile + 64) of a slab whose last row ends `end` bytes after
   // its start; rows past the end read 0
@@ -121,9 +150,11 @@ struct BwdCopy {
     const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xffffu)),
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(end - off)), (uint32_t)kBufferFlags};
+    if constexpr (NWC < NW)
+      if (wave >= NWC) return;  // wave-uniform
     const uint32_t l0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_addr(dst) + BS * wave));
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) dma16(rs, l0 + BS * NW * j, lane_src + step * j);
+    for (int j = 0; j < CPW; ++j) dma16(rs, l0 + BS * NWC * j, lane_src + step * j);
   }
 };
 
@@ -171,7 +202,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int n_kv = (Lk + BC - 1) / BC;
   if constexpr (CAUSAL) n_kv = min(n_kv, (min(i0 + BR, Lq) - 1 + off) / BC + 1);
 
-  const BwdCopy<D, NW> cpk(wave, lane, p.sl[T_K]), cpv(wave, lane, p.sl[T_V]);
+  // the tile copies are issued by waves 0-3, one per SIMD (waves w and w+4 share
+  // a SIMD): the other wave of each SIMD is not held up by the copy burst after
+  // each barrier, as in the forward kernel
+  const BwdCopy<D, NW, 4> cpk(wave, lane, p.sl[T_K]), cpv(wave, lane, p.sl[T_V]);
   auto copies = [&](int t, int st) {
     cpk.template copy<KBS>(kslab, end_k, t, st ? kr1 : kr0);
     cpk.template copy<VBS>(kslab, end_k, t, st ? kt1 : kt0);
@@ -320,18 +354,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     bwd_wait_join();
   }
 
-  // epilogue: dQ = scale·dQᵀ; lane holds dims 32nb + 8(r/4) + 4g + r%4 of row qrow
+  // epilogue: dQ = scale·dQᵀ; lane holds dims 32nb + 8(r/4) + 4g + r%4 of row qrow.
+  // The wave's 32 rows go row-major through LDS (free since the last barrier)
+  // and out as whole rows, 16 bytes per lane (see stage_rows_out)
   const auto ors = make_rsrc(bwd_slab((char*)p.dq, p, T_DQ, bh), bwd_end<D>(p, T_DQ, Lq));
-  const float sc = p.scale;
+  if constexpr (D == 128) {
+    // waves 0-3 two to a transposing K stage, waves 4-7 one to each row stage
+    static_assert(2 * 32 * (2 * D + 16) <= VT && 32 * (2 * D + 16) <= KT, "staging fits");
+    unsigned char* const stg = wave < 4 ? (wave < 2 ? kt0 : kt1) + (wave & 1) * 32 * (2 * D + 16)
+                                        : (wave == 4 ? kr0 : wave == 5 ? kr1 : wave == 6 ? vr0 : vr1);
+    stage_rows_out<D, DT>(dq, p.scale, stg, lane, ors, i0w, p.sl[T_DQ]);
+  } else {
+    // (at D = 64 the six stages cannot take eight waves' rows: direct 8-byte stores)
+    const float sc = p.scale;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = 32 * nb + 8 * q4 + 4 * g;
-      const u32x2 w = {pack2<DT>(dq[nb][4 * q4] * sc, dq[nb][4 * q4 + 1] * sc),
-                       pack2<DT>(dq[nb][4 * q4 + 2] * sc, dq[nb][4 * q4 + 3] * sc)};
-      buf_store8(ors, (uint32_t)(qrow * p.sl[T_DQ] + d0) * 2, w);  // rows >= Lq are dropped
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * nb + 8 * q4 + 4 * g;
+        const u32x2 w = {pack2<DT>(dq[nb][4 * q4] * sc, dq[nb][4 * q4 + 1] * sc),
+                         pack2<DT>(dq[nb][4 * q4 + 2] * sc, dq[nb][4 * q4 + 3] * sc)};
+        buf_store8(ors, (uint32_t)(qrow * p.sl[T_DQ] + d0) * 2, w);  // rows >= Lq are dropped
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -568,22 +613,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     bwd_wait_join();
   }
 
-  // epilogue: lane holds dims 32nb + 8(r/4) + 4g + r%4 of key `key`
+  // epilogue: lane holds dims 32nb + 8(r/4) + 4g + r%4 of key `key`; each wave's
+  // 32 rows of dK and of dV go row-major through two LDS stages (free since the
+  // last barrier) and out as whole rows (see stage_rows_out)
   const auto dkrs = make_rsrc(bwd_slab((char*)p.dk, p, T_DK, bh), bwd_end<D>(p, T_DK, Lk));
   const auto dvrs = make_rsrc(bwd_slab((char*)p.dv, p, T_DV, bh), bwd_end<D>(p, T_DV, Lk));
-  const float sc = p.scale;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = 32 * nb + 8 * q4 + 4 * g;
-      const u32x2 wk = {pack2<DT>(dk[nb][4 * q4] * sc, dk[nb][4 * q4 + 1] * sc),
-                        pack2<DT>(dk[nb][4 * q4 + 2] * sc, dk[nb][4 * q4 + 3] * sc)};
-      const u32x2 wv = {pack2<DT>(dv[nb][4 * q4], dv[nb][4 * q4 + 1]),
-                        pack2<DT>(dv[nb][4 * q4 + 2], dv[nb][4 * q4 + 3])};
-      buf_store8(dkrs, (uint32_t)(key * p.sl[T_DK] + d0) * 2, wk);  // keys >= Lk are dropped
-      buf_store8(dvrs, (uint32_t)(key * p.sl[T_DV] + d0) * 2, wv);
-    }
+  static_assert(32 * (2 * D + 16) <= KT, "staging fits");
+  unsigned char* const stk = wave == 0 ? qr0 : wave == 1 ? qr1 : wave == 2 ? or0 : or1;
+  unsigned char* const stv = wave == 0 ? qt0 : wave == 1 ? qt1 : wave == 2 ? ot0 : ot1;
+  stage_rows_out<D, DT>(dk, p.scale, stk, lane, dkrs, j0w, p.sl[T_DK]);
+  stage_rows_out<D, DT>(dv, 1.0f, stv, lane, dvrs, j0w, p.sl[T_DV]);
 }
 
 }  // namespace fa355
