@@ -449,7 +449,10 @@ def test_causal_bottom_right(B, H, Lq, Lk, D, dtype):
 SPLIT_CASES = [(1, 2, 300, 300, 128, "bf16", True, 2), (1, 2, 300, 300, 128, "bf16", True, 8),
                (2, 2, 200, 1000, 64, "fp16", False, 3), (1, 2, 100, 2000, 128, "fp16", True, 5),
                (1, 1, 1, 4096, 128, "bf16", False, 16), (1, 3, 513, 513, 64, "bf16", True, 4),
-               (1, 2, 130, 65, 128, "fp16", False, 64)]
+               (1, 2, 130, 65, 128, "fp16", False, 64),
+               # few rows, many splits (the per-row merge): D = 64 with 16 lane groups and a split count that
+               # is not a multiple of them; 50 splits over 11 key tiles (empty splits), 8 per lane group
+               (1, 4, 3, 2000, 64, "bf16", True, 40), (2, 2, 16, 700, 128, "fp16", False, 50)]
 
 
 @pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal,splits", SPLIT_CASES,

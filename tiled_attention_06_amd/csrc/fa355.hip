@@ -52,6 +52,20 @@ int launch(const fa355::FwdParams& p, const fa355::MergeParams& m, hipStream_t s
   if (st != FA_OK || p.n_split == 1) return st;
   constexpr int rows_per_block = 256 / (D / 4);
   const int64_t rows = (int64_t)m.bh * m.Lq;
+  // Few rows (under one workgroup per CU with the batched merge) and enough
+  // splits to share among a row's lane groups: one workgroup per row, each lane
+  // group taking up to 8 splits in one batch of loads.
+  constexpr int NG = 256 / (D / 4);
+  if (rows * 8 <= 2048 && m.n_split >= 8 && m.n_split <= 8 * NG) {
+    const dim3 wgrid((unsigned)rows);
+    if (m.n_split <= 2 * NG)
+      hipLaunchKernelGGL((fa355::fa_merge_wide_kernel<D, DT, 2>), wgrid, dim3(256), 0, stream, m);
+    else if (m.n_split <= 4 * NG)
+      hipLaunchKernelGGL((fa355::fa_merge_wide_kernel<D, DT, 4>), wgrid, dim3(256), 0, stream, m);
+    else
+      hipLaunchKernelGGL((fa355::fa_merge_wide_kernel<D, DT, 8>), wgrid, dim3(256), 0, stream, m);
+    return launch_status();
+  }
   const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
   // splits merged per batch of loads: as many as there are, up to 16 (a batch
   // larger than the split count only adds predicated-off slots and registers)

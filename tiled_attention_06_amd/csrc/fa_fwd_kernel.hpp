@@ -1026,4 +1026,74 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
   if (d0 == 0) p.lse[r] = (M + log2f(lf)) * 0.69314718055994530942f;
 }
 
+// Merge for grids of few rows and many splits (a decode step: a handful of rows,
+// tens of splits): one workgroup per row.  Its NG = 256 / (D/4) lane groups each
+// combine the splits g, g+NG, g+2·NG, ... (at most MB of them, their loads issued
+// together) into a partial (max, sums and output relative to it), and group 0
+// combines the NG partials through LDS with the same streaming update.  One round
+// trip to memory instead of one per batch of splits; exact like the batched merge,
+// only the order of the fp32 additions differs.
+template <int D, int DT, int MB>
+__global__ __launch_bounds__(256) void fa_merge_wide_kernel(MergeParams p) {
+  constexpr int LPR = D / 4, NG = 256 / LPR;
+  __shared__ float sml[NG][4];
+  __shared__ f32x4 sacc[NG][LPR];
+  const int tid = threadIdx.x, grp = tid / LPR, lg = tid % LPR, d0 = lg * 4;
+  const int64_t r = blockIdx.x;  // row over B*H*Lq
+  const int bh = (int)(r / p.Lq), i = (int)(r - (int64_t)bh * p.Lq);
+  const size_t stride = (size_t)p.bh * p.Lq;  // rows per split
+  f32x4 st[MB], x[MB];
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    const int s = grp + NG * u;
+    if (s < p.n_split) {
+      const size_t row = (size_t)s * stride + r;
+      st[u] = *(const f32x4*)(p.ws_ml + row * 4);
+      x[u] = *(const f32x4*)(p.ws_o + row * D + d0);
+    }
+  }
+  // a group without splits keeps M below every split's max and zero sums
+  float M = -3.0e38f;
+#pragma unroll
+  for (int u = 0; u < MB; ++u)
+    if (grp + NG * u < p.n_split) M = fmaxf(M, st[u][0]);
+  float lf = 0.f, lr = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    if (grp + NG * u < p.n_split) {
+      const float w = __builtin_amdgcn_exp2f(st[u][0] - M);
+      lf += w * st[u][1];
+      lr += w * st[u][2];
+      acc += w * x[u];
+    }
+  }
+  if (lg == 0) {
+    sml[grp][0] = M;
+    sml[grp][1] = lf;
+    sml[grp][2] = lr;
+  }
+  sacc[grp][lg] = acc;
+  __syncthreads();
+  if (grp != 0) return;
+  float Mt = sml[0][0];
+#pragma unroll
+  for (int gi = 1; gi < NG; ++gi) Mt = fmaxf(Mt, sml[gi][0]);
+  lf = 0.f;
+  lr = 0.f;
+  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const float w = __builtin_amdgcn_exp2f(sml[gi][0] - Mt);
+    lf += w * sml[gi][1];
+    lr += w * sml[gi][2];
+    acc += w * sacc[gi][lg];
+  }
+  const float inv = 1.0f / lr;
+  const int b = bh / p.H, h = bh - b * p.H;
+  char* const orow = (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)i * p.o_sl + d0) * 2;
+  *(u32x2*)orow = u32x2{pack2<DT>(acc[0] * inv, acc[1] * inv), pack2<DT>(acc[2] * inv, acc[3] * inv)};
+  if (d0 == 0) p.lse[r] = (Mt + log2f(lf)) * 0.69314718055994530942f;
+}
+
 }  // namespace fa355
