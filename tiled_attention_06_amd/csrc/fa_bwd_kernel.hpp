@@ -176,6 +176,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NBLK = G::NBLK, KBS = G::KBS, VBS = G::VBS, KT = G::KT, VT = G::VT;
   // per stage: K row image, K transposing image, V row image
   __shared__ __attribute__((aligned(16))) unsigned char kr0[KT], kr1[KT], kt0[VT], kt1[VT], vr0[KT], vr1[KT];
+  // dropout: per wave and 32-key half, the buffer of the Philox words' quad transpose
+  __shared__ __attribute__((aligned(16))) uint32_t dxp[DROP ? 8 * 2 * 320 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -297,10 +299,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const u32x4 mine =
               drop_block((j0 + 32 * kb + 16 * (j >> 1) + 8 * (j & 1) + 4 * g) >> 2, qrow >> 2, bh, p.seed_lo,
                          p.seed_hi);
-          uint32_t wd[4] = {mine[0], mine[1], mine[2], mine[3]};
-          quad_transpose(wd, j);
+          // quad transpose through LDS, as in the forward kernel: word i of lane (quad q, j)
+          // at dword 20q + 4i + j of this wave's buffer for half kb, then 16 bytes at 20q + 4j
+          uint32_t* const xb = dxp + (wave * 2 + kb) * 320 + 20 * (lane >> 2);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) words[4 * kb + i] = wd[i];
+          for (int i = 0; i < 4; ++i) xb[4 * i + j] = mine[i];
+          const u32x4 got = *(const u32x4*)(xb + 4 * j);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) words[4 * kb + i] = got[i];
         }
       }
       u32x4 db[KB][2];
@@ -393,6 +399,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // per stage: LSE·log2(e) and Δ of the tile's 64 rows (a 1 KB copy each; the
   // first 256 bytes are used)
   __shared__ __attribute__((aligned(16))) float ls0[256], ls1[256], de0[256], de1[256];
+  // dropout: per wave and 32-row half, the exchange buffer of the Philox blocks (64 lanes x 16 bytes)
+  __shared__ __attribute__((aligned(16))) uint32_t dxk[DROP ? 4 * 2 * 256 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -517,9 +525,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto drop_half = [&](int qb, int i0, u32x4 (&blk)[4]) {
     const int j = lane & 3, h = j >> 1, a = j & 1;
     const u32x4 mine = drop_block(key >> 2, (i0 + 32 * qb + 16 * h + 8 * a + 4 * g) >> 2, bh, p.seed_lo, p.seed_hi);
+    // the exchange goes through LDS: each lane stores its block (16 bytes, the wave's
+    // 64 lanes contiguous), then reads its quad's four blocks (the quad's lanes read
+    // the same addresses: broadcasts)
+    u32x4* const xb = (u32x4*)(dxk + (wave * 2 + qb) * 256) + 4 * (lane >> 2);
+    xb[j] = mine;
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-      blk[x] = u32x4{quad_bcast(mine[0], x), quad_bcast(mine[1], x), quad_bcast(mine[2], x), quad_bcast(mine[3], x)};
+    for (int x = 0; x < 4; ++x) blk[x] = xb[x];
   };
   // dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS for register half h, dims block nb of half qb
   auto grad_mfma = [&](int qb, int h, int nb, const u32x4 (&pb)[2], const u32x4 (&db)[2],
