@@ -155,42 +155,6 @@ template <bool B3 = true>
 __device__ __forceinline__ u32x4 drop_block(int key4, int row4, int bh, uint32_t k0, uint32_t k1) {
   return philox10<B3>((uint32_t)key4, (uint32_t)row4, (uint32_t)bh, 0u, k0, k1);
 }
-// Word w (the same register in every lane) of lane s of each quad of lanes
-// (quad_perm(s, s, s, s); s is a constant wherever the callers are unrolled).
-template <int S>
-__device__ __forceinline__ uint32_t quad_bcast_c(uint32_t w) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, S * 0x55, 0xf, 0xf, false);
-}
-__device__ __forceinline__ uint32_t quad_bcast(uint32_t w, int s) {
-  switch (s) {
-    case 0: return quad_bcast_c<0>(w);
-    case 1: return quad_bcast_c<1>(w);
-    case 2: return quad_bcast_c<2>(w);
-    default: return quad_bcast_c<3>(w);
-  }
-}
-// 4 x 4 transpose within each quad of lanes (j = lane & 3): lane j holds v[0..3],
-// the four words of one Philox block; afterwards v[s] is word j of the block lane
-// s held.  Two butterfly stages (partners j^1, then j^2); in each, a lane sends
-// the element of every register pair it does not keep and takes its partner's.
-__device__ __forceinline__ void quad_transpose(uint32_t (&v)[4], int j) {
-  const bool b0 = (j & 1) != 0, b1 = (j & 2) != 0;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {  // pairs (0,1), (2,3); quad_perm(1,0,3,2)
-    const uint32_t send = b0 ? v[2 * q] : v[2 * q + 1];
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xf, 0xf, false);
-    v[2 * q] = b0 ? recv : v[2 * q];
-    v[2 * q + 1] = b0 ? v[2 * q + 1] : recv;
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {  // pairs (0,2), (1,3); quad_perm(2,3,0,1)
-    const uint32_t send = b1 ? v[q] : v[q + 2];
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0x4E, 0xf, 0xf, false);
-    v[q] = b1 ? recv : v[q];
-    v[q + 2] = b1 ? v[q + 2] : recv;
-  }
-}
-
 // 16-bit lane masks of the kept weights of word w's bytes b0 and b0+1
 __device__ __forceinline__ uint32_t keep_pair(uint32_t w, int b0, uint32_t T) {
   const uint32_t lo = (w >> (8 * b0)) & 0xffu, hi = (w >> (8 * b0 + 8)) & 0xffu;
