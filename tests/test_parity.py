@@ -190,6 +190,31 @@ def test_geometry_forms(D, dtype, causal):
         assert torch.equal(o_all[:, :4, 0].cpu(), few["v"][:, :, 0])
 
 
+@pytest.mark.parametrize("H,L,D,dtype,causal", [
+    (32, 2048, 128, "fp16", True),   # 512 items: XCD blocks of 64 items, two head pairs each
+    (18, 1900, 128, "bf16", True),   # 270 items in one block (270 is no multiple of 16)
+    (19, 1900, 64, "bf16", False),   # 285 items: the middle one runs alone
+])
+def test_paired_form(H, L, D, dtype, causal):
+    # Two-key-group grids with more items than CUs (256 on this GPU) run two items per
+    # workgroup, a heavy causal query tile and then a light one, the second one's Q rows and
+    # first K tiles requested while the first one's results are merged and stored.  A row's
+    # result does not depend on that: the first heads alone (at most 256 items, one per
+    # workgroup) reproduce those heads bit for bit, and both match the oracle.
+    inp = ai.make_custom(1, H, L, L, D, dtype, causal, seed=37_000 + H)
+    note(f"paired form B1 H{H} L{L} D{D} {dtype} causal={causal}")
+    n = H // 2
+    sub = {**inp, **{x: inp[x][:, :n].contiguous() for x in ("q", "k", "v")}}
+    o_all, l_all = run_gpu(inp)
+    o_sub, l_sub = run_gpu(sub)
+    assert torch.equal(o_all[:, :n], o_sub) and torch.equal(l_all[:, :n], l_sub), \
+        "two-key-group form: result depends on the pairing of items"
+    heads = [0, H - 1]
+    pick = {**inp, **{x: inp[x][:, heads].contiguous() for x in ("q", "k", "v")}}
+    O_ref, L_ref = attention_fp64(pick["q"], pick["k"], pick["v"], inp["scale"], causal)
+    compare(o_all[:, heads], l_all[:, heads], O_ref, L_ref, dtype, "paired form", src=pick)
+
+
 # ------------------------------------------------------------------------------------------
 # the five workloads at full size, in the launch configuration the bench times
 # ------------------------------------------------------------------------------------------

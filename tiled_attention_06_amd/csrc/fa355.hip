@@ -190,18 +190,30 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   // would not exceed the CU count takes 128 rows per workgroup instead, with the
   // 8 waves in two key groups that take alternate key tiles: twice the
   // workgroups, the heaviest causal ones half as long, and still two waves per
-  // SIMD.
+  // SIMD.  When those items outnumber the CUs (and without dropout), each
+  // workgroup runs two of them, from both ends of its XCD's block of items (the
+  // whole grid when the item count is no multiple of 16): a heavy causal tile
+  // and then a light one, whose sum is the same for every workgroup when a block
+  // holds whole pairs of heads (causal grids are paired only then).  The second
+  // item's first loads overlap the first one's merge and stores, and no
+  // workgroup is launched twice on a CU.
   const int BR8 = fa355::Geo<128>::BR;
   static_assert(fa355::Geo<64>::BR == fa355::Geo<128>::BR && fa355::Geo<64, 8, 2>::BR == fa355::Geo<128, 8, 2>::BR,
                 "row tile independent of D");
   int64_t n_qt = ((int64_t)Lq + BR8 - 1) / BR8;
   bool narrow = false;
+  int n_rep = 1;
   if (splits == 1 && (int64_t)B * H * n_qt <= 2048) {
     const int cus = cu_count();
     narrow = cus > 0 && (int64_t)B * H * n_qt <= cus;
+    if (narrow) {
+      n_qt = ((int64_t)Lq + fa355::Geo<128, 8, 2>::BR - 1) / fa355::Geo<128, 8, 2>::BR;
+      const int64_t n_items = (int64_t)B * H * n_qt;
+      const int64_t per_block = n_items % 16 == 0 ? n_items / 8 : n_items;
+      if (drop_t >= 256 && n_items > cus && (!causal || per_block % (2 * n_qt) == 0)) n_rep = 2;
+    }
   }
-  if (narrow) n_qt = ((int64_t)Lq + fa355::Geo<128, 8, 2>::BR - 1) / fa355::Geo<128, 8, 2>::BR;
-  const int64_t num_wg = (int64_t)B * H * n_qt * splits;
+  const int64_t num_wg = n_rep == 2 ? ((int64_t)B * H * n_qt + 1) / 2 : (int64_t)B * H * n_qt * splits;
   if ((int64_t)B * H >= (1ll << 31) || num_wg >= (1ll << 22)) return FA_ERR_SHAPE;
 
   if (splits > 1 && use_scratch) {  // every argument is valid: now the one HIP query
@@ -230,7 +242,8 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   p.bh = (int)((int64_t)B * H);
   p.ws_o = splits > 1 ? (float*)ws : nullptr;
   p.ws_ml = splits > 1 ? (float*)((char*)ws + ws_o_bytes(B, H, Lq, D, splits)) : nullptr;
-  p.xcd_remap = (num_wg % 8 == 0) ? 1 : 0;
+  p.xcd_remap = (n_rep == 2 ? ((int64_t)B * H * n_qt) % 16 == 0 : num_wg % 8 == 0) ? 1 : 0;
+  p.n_rep = n_rep;
   // The softmax runs in base 2 with the scale folded into one positive factor;
   // a negative scale negates Q (exact in fp16/bf16) and a zero scale zeroes it.
   const double log2e = 1.4426950408889634074;

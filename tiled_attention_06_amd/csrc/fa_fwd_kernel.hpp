@@ -105,6 +105,7 @@ struct FwdParams {
   float* ws_o;      // n_split > 1: unnormalised partial outputs, fp32 [n_split][B*H][Lq][D]
   float* ws_ml;     // n_split > 1: per row (m, l_f, l_r, 0), fp32 [n_split][B*H][Lq][4]
   int xcd_remap;    // 1: group consecutive work items on one XCD
+  int n_rep;        // work items per workgroup: 1, or 2 (paired form, two key groups only)
   float c;          // |scale| * log2(e), or log2(e) when scale == 0 (always > 0)
   uint32_t q_and;   // 0xffffffff, or 0 when scale == 0 (Q forced to zero)
   uint32_t q_xor;   // 0x80008000 when scale < 0 (Q negated exactly), else 0
@@ -255,6 +256,21 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// The kernel's argument block read afresh from the kernel-argument segment (the
+// explicit arguments start at its offset 0).  The empty asm hides the segment
+// address, so that a loop over work items reads the arguments again in each
+// iteration instead of keeping all of them in scalar registers across it.
+template <class T>
+__device__ __forceinline__ T reread_args() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint64_t a = (uint64_t)(uintptr_t)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(a));
+  return *(const __attribute__((address_space(4))) T*)a;
+#else
+  return T{};
+#endif
+}
+
 // max / sum of a value over lanes l and l^32 (every lane gets the result)
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -307,7 +323,7 @@ struct Geo {
 };
 
 template <int D, int DT, bool CAUSAL, bool DROP, int NW = 8, int KG = 1>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(FwdParams args) {
   using G = Geo<D, NW, KG>;
   constexpr int BC = G::BC, KB = G::KB, NB = G::NB, KS = G::KS, NCH = G::NCH;
   constexpr int NBLK = G::NBLK, KBS = G::KBS, VBS = G::VBS, KT = G::KT, VT = G::VT;
@@ -343,36 +359,67 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) uint32_t dxp[DROP ? NW * 2 * 320 : 4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, g = lane >> 5;
 
   // ---- work item: (batch*head, query tile); heaviest causal tiles first, and
   // consecutive items (all query tiles of one head) on one XCD, whose L2 then
   // serves the K/V re-reads of that head.
   const int bid = blockIdx.x;
-  const int item_s = p.xcd_remap ? (bid & 7) * (p.num_wg >> 3) + (bid >> 3) : bid;
-  // the key splits of one (batch*head, query tile) are consecutive items
-  const int item = item_s / p.n_split, split = item_s - item * p.n_split;
-  int bh, qt_r;
-  if (CAUSAL) {
-    // Heads in pairs, and within a pair the query tiles of both heads heaviest
-    // first: work is then dispatched nearly longest-first while only two heads'
-    // K/V are streamed at a time on each XCD (an odd last head runs alone).
-    const int g = item / (2 * p.n_qt), j = item - g * 2 * p.n_qt;
-    if (2 * g + 1 < p.bh) {
-      bh = 2 * g + (j & 1);
-      qt_r = j >> 1;
+  // Two items per workgroup (the paired form) only in the two-key-group kernels
+  // without dropout; the dropout kernels have no scalar registers to spare for
+  // the loop.
+  constexpr bool PAIRABLE = KG == 2 && !DROP;
+  const int n_rep = PAIRABLE ? args.n_rep : 1;
+  // Q rows of the current item as loaded (the sign / zero transform of the scale
+  // is applied once they are in)
+  u32x4 qr[G::KS];
+  for (int rep = 0; rep < n_rep; ++rep) {
+  const FwdParams p = PAIRABLE ? reread_args<FwdParams>() : args;
+  // Item r of this workgroup: batch*head, query tile counted from the heaviest,
+  // key split; false if there is none.  Paired form (n_rep == 2): the items of an
+  // XCD's block (all of the block when the grid is not spread over the XCDs) are
+  // taken from both ends, the first from the start and the second from the end,
+  // so that a workgroup runs a heavy causal tile and then a light one.
+  auto locate = [&](const FwdParams& pa, int r, int& bh_, int& qtr_, int& split_) -> bool {
+    int item_s;
+    if (PAIRABLE && n_rep == 2) {
+      const int nb = pa.xcd_remap ? 8 : 1;
+      const int x = bid % nb, i = bid / nb, mi = pa.bh * pa.n_qt / nb;
+      if (r && mi - 1 - i == i) return false;  // the middle item of an odd block runs once
+      item_s = x * mi + (r ? mi - 1 - i : i);
     } else {
-      bh = 2 * g;
-      qt_r = j;
+      item_s = pa.xcd_remap ? (bid & 7) * (pa.num_wg >> 3) + (bid >> 3) : bid;
     }
-  } else {
-    bh = item / p.n_qt;
-    qt_r = item - bh * p.n_qt;
-  }
-  bh = __builtin_amdgcn_readfirstlane(bh);  // uniform: keep it in scalar registers
-  qt_r = __builtin_amdgcn_readfirstlane(qt_r);
+    // the key splits of one (batch*head, query tile) are consecutive items
+    const int item = item_s / pa.n_split;
+    split_ = item_s - item * pa.n_split;
+    if (CAUSAL) {
+      // Heads in pairs, and within a pair the query tiles of both heads heaviest
+      // first: work is then dispatched nearly longest-first while only two heads'
+      // K/V are streamed at a time on each XCD (an odd last head runs alone).
+      const int hp = item / (2 * pa.n_qt), j = item - hp * 2 * pa.n_qt;
+      if (2 * hp + 1 < pa.bh) {
+        bh_ = 2 * hp + (j & 1);
+        qtr_ = j >> 1;
+      } else {
+        bh_ = 2 * hp;
+        qtr_ = j;
+      }
+    } else {
+      bh_ = item / pa.n_qt;
+      qtr_ = item - bh_ * pa.n_qt;
+    }
+    bh_ = __builtin_amdgcn_readfirstlane(bh_);  // uniform: keep it in scalar registers
+    qtr_ = __builtin_amdgcn_readfirstlane(qtr_);
+    return true;
+  };
+  int bh, qt_r, split;
+  if (!locate(p, rep, bh, qt_r, split)) break;
+  // thread-derived values taken afresh for each item (see opaque()): derived once
+  // before the loop, they and what the compiler computes from them would stay
+  // live across all of it
+  const int lane = opaque(tid) & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(opaque(tid) >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
   const int qt = CAUSAL ? p.n_qt - 1 - qt_r : qt_r;
   const int i0 = qt * G::BR;
   // rows of this wave; with two key groups, waves w and w + NW/2 share rows
@@ -383,13 +430,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // (batch, head) slabs; a slab's rows are q_sl (k_sl, ...) elements apart and its
   // buffer range ends with the last row, so rows past the end read 0 / drop stores
-  const int bb = __builtin_amdgcn_readfirstlane(bh / p.H), hh = bh - bb * p.H;
+  auto slab = [&](const void* base, int64_t sb, int64_t sh, int H, int bh_) -> const char* {
+    const int b_ = __builtin_amdgcn_readfirstlane(bh_ / H), h_ = bh_ - b_ * H;
+    return (const char*)base + ((int64_t)b_ * sb + (int64_t)h_ * sh) * 2;
+  };
   const int q_sl = p.q_sl, k_sl = p.k_sl, v_sl = p.v_sl, o_sl = p.o_sl;
-  const char* const qslab = (const char*)p.q + ((int64_t)bb * p.q_sb + (int64_t)hh * p.q_sh) * 2;
-  const char* const kslab = (const char*)p.k + ((int64_t)bb * p.k_sb + (int64_t)hh * p.k_sh) * 2;
-  const char* const vslab = (const char*)p.v + ((int64_t)bb * p.v_sb + (int64_t)hh * p.v_sh) * 2;
-  char* const oslab = (char*)p.o + ((int64_t)bb * p.o_sb + (int64_t)hh * p.o_sh) * 2;
-  const auto qrs = make_rsrc(qslab, (uint32_t)((Lq - 1) * q_sl + D) * 2);
+  const char* const kslab = slab(p.k, p.k_sb, p.k_sh, p.H, bh);
+  const char* const vslab = slab(p.v, p.v_sb, p.v_sh, p.H, bh);
+  char* const oslab = (char*)slab(p.o, p.o_sb, p.o_sh, p.H, bh);
+  const uint32_t end_q = (uint32_t)((Lq - 1) * q_sl + D) * 2;
   const auto ors = make_rsrc(oslab, (uint32_t)((Lq - 1) * o_sl + D) * 2);
 
   // ---- HBM -> LDS copy of one tile.  Copy j of wave w < NWC fills block b = w + NWC·j:
@@ -435,11 +484,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // Causal (bottom-right): query row i sits at key position i + off, key j is
   // visible to it iff j <= i + off.
   const int off = CAUSAL ? p.kv_off : 0;
-  int n_kv = (Lk + BC - 1) / BC;
-  if constexpr (CAUSAL) {
-    const int last_row = min(i0 + G::BR, Lq) - 1;
-    n_kv = min(n_kv, (last_row + off) / BC + 1);
-  }
+  auto kv_tiles = [&](int i0_) {  // key tiles seen by the rows from i0_ on
+    int n = (Lk + BC - 1) / BC;
+    if constexpr (CAUSAL) n = min(n, (min(i0_ + G::BR, Lq) - 1 + off) / BC + 1);
+    return n;
+  };
+  const int n_kv = kv_tiles(i0);
   // this item's tiles: [t_b, t_e), an equal share of the n_kv tiles per split
   const int t_b = __builtin_amdgcn_readfirstlane((int)((int64_t)split * n_kv / p.n_split));
   const int t_e = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * n_kv / p.n_split));
@@ -449,19 +499,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // ---- Q tile -> VGPRs, as the B operand of Sᵀ = K·Qᵀ (column = query row l%32,
   // contraction slots of half g = head dims 16s+8g .. 16s+8g+7).  Rows past Lq read 0.
-  const int qrow = i0w + l32;
-  u32x4 qr[KS];
+  auto load_q = [&](const char* qslab_, int i0w_) {
+    const auto rs = make_rsrc(qslab_, end_q);
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const u32x4 x = buf_load16(qrs, (uint32_t)(qrow * q_sl + 16 * s + 8 * g) * 2);
-    qr[s] = (x & p.q_and) ^ p.q_xor;
-  }
+    for (int s = 0; s < KS; ++s) qr[s] = buf_load16(rs, (uint32_t)((i0w_ + l32) * q_sl + 16 * s + 8 * g) * 2);
+  };
+  auto fix_q = [&]() {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qr[s] = (qr[s] & p.q_and) ^ p.q_xor;
+  };
   // stage of tile t: (t - t_b) % NS.  Only what the first Sᵀ needs is copied
   // before the first wait (K of tile t_b, and with two key groups of t_b+1 too);
-  // the other first tiles follow once it is in, while that Sᵀ is computed.
-  if (t_b < t_e) copy_k(t_b, I0{});
-  if constexpr (KG == 2)
-    if (t_b + 1 < t_e) copy_k(t_b + 1, std::integral_constant<int, 1>{});
+  // the other first tiles follow once it is in, while that Sᵀ is computed.  The
+  // second item of a pair had its Q rows and those K tiles requested while the
+  // first one finished.
+  if (rep == 0) {
+    load_q(slab(p.q, p.q_sb, p.q_sh, p.H, bh), i0w);
+    if (t_b < t_e) copy_k(t_b, I0{});
+    if constexpr (KG == 2)
+      if (t_b + 1 < t_e) copy_k(t_b + 1, std::integral_constant<int, 1>{});
+  }
 
   // per-lane LDS offsets of the MFMA operand reads.  Tile row r sits in block
   // r % NBLK at position r / NBLK; rows r and r + 8m (m >= 0, r < 8) differ by a
@@ -673,6 +730,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
   if constexpr (KG == 1) {
     wait_join();  // Q and K of tile t_b are in
+    fix_q();
     // V of tile t_b, then K and V of tiles t_b+1 and t_b+2, in the order the loop
     // needs them (the steps copy tile t+3 in step t)
     if (t_b < t_e) copy_v(t_b, I0{});
@@ -786,6 +844,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // (whose Sᵀ was made one step earlier) and V of tiles t_b+2s+2 and +3 into the
     // stages of the previous step's tiles (whose PV ran one step earlier).
     wait_join();  // Q and K of tiles t_b, t_b+1 are in
+    fix_q();
     // V of tiles t_b, t_b+1 and K of tiles t_b+2, t_b+3 while the first Sᵀ is made
     if (t_b < t_e) copy_v(t_b, I0{});
     if (t_b + 1 < t_e) copy_v(t_b + 1, std::integral_constant<int, 1>{});
@@ -852,7 +911,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       xst[wr][2][lane] = l_r;
     }
     __syncthreads();
-    if (kg == 1) return;
+    // Paired form: Q rows and the first two K tiles of the next item are requested
+    // now (its first tile is tile 0, stage 0; the K stages are free once every wave
+    // passed the barrier above), and land while this item's results are merged
+    // and stored; the output rows are staged in the V stages for that.
+    if (PAIRABLE && n_rep == 2 && rep == 0) {
+      // (the arguments read once more: kept from the top of the item, they would
+      // stay in scalar registers across all of it)
+      const FwdParams pn = reread_args<FwdParams>();
+      int bh2, qtr2, split2;
+      if (locate(pn, 1, bh2, qtr2, split2)) {
+        const int i02 = (CAUSAL ? pn.n_qt - 1 - qtr2 : qtr2) * G::BR;
+        load_q(slab(pn.q, pn.q_sb, pn.q_sh, pn.H, bh2), i02 + 32 * wr);
+        const char* const kslab2 = slab(pn.k, pn.k_sb, pn.k_sh, pn.H, bh2);
+        const int te2 = kv_tiles(i02);
+        constexpr auto KBSc = std::integral_constant<int, KBS>{};
+        if (te2 > 0) copy_tile(kslab2, tb_k, end_k, step_k, src_k, ks0, 0, KBSc);
+        if (te2 > 1) copy_tile(kslab2, tb_k, end_k, step_k, src_k, ks1, 1, KBSc);
+      }
+    }
+    if (kg == 1) continue;
     if (live) {
       const float m1 = xst[wr][0][lane];
       const float mm = fmaxf(m_run, m1);
@@ -895,21 +973,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const u32x4 st = {__float_as_uint(m_run), __float_as_uint(lf_t), __float_as_uint(lr_t), 0u};
       *(u32x4*)(p.ws_ml + (part * Lq + row_e) * 4) = st;
     }
-    return;
+    continue;
   }
   // one pass: normalise by the sum of the rounded weights, store O and LSE.  The
   // accumulator layout gives a lane 4 dims of one row per 8 bytes, scattered over
   // 32 rows per instruction; the wave first lays its 32 rows out row-major in an
   // LDS stage of the ring (free since the last barrier: every copy has landed and
-  // every read is done; one stage per wave, and with two key groups only group 0,
-  // waves 0..3, gets here, after group 1's hand-over through the V stages), then
-  // stores whole rows, 16 bytes per lane.  Rows are OPITCH bytes apart in LDS
+  // every read is done; one stage per wave.  With two key groups only group 0,
+  // waves 0..3, gets here, and wave w uses V stage w, whose hand-over from its
+  // partner it has just read: the K stages may be filling for the next item),
+  // then stores whole rows, 16 bytes per lane.  Rows are OPITCH bytes apart in LDS
   // (16 bytes of pad: 16-byte aligned row reads, and the 8-byte writes of lanes
   // 0..15 on distinct banks).
   const float inv = DROP ? p.drop_scale / lr_t : 1.0f / lr_t;
   constexpr int OPITCH = 2 * D + 16;
   static_assert(32 * OPITCH <= KT && 32 * OPITCH <= VT, "one wave's output rows fit a stage");
-  unsigned char* const stg = wave < 4 ? kst_rt(wave) : vst_rt(wave - 4);
+  unsigned char* const stg = KG == 2 ? vst_rt(wr) : wave < 4 ? kst_rt(wave) : vst_rt(wave - 4);
   const int l32_e = lane_e & 31;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -930,6 +1009,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     buf_store16(ors, (uint32_t)((i0w + r) * o_sl + ch * 8) * 2, x);  // rows >= Lq are dropped
   }
   if (g_e == 0 && row_e < Lq) p.lse[(size_t)bh * Lq + row_e] = (m_run + log2f(lf_t)) * 0.69314718055994530942f;
+  }
 }
 
 // ---- merge of key splits ([DF §2.2], second layer, applied across splits: the
