@@ -21,8 +21,12 @@ the stored O and LSE of a forward pass:
   P_ij  = fl32(2^(S_ij·c − LSE_i·log2 e)),  c = fl32(scale·log2 e)
   Δ_i   = fl32(Σ_d dO_id·O_id) from the stored O
   dV_j  = round(Σ_i round(P_ij)·dO_i),  dP_ij = fl32(dO_i·v_j)
-  dS_ij = round(fl32(P_ij·(dP_ij − Δ_i)))
+  dS_ij = round(fl32(W_ij·(dP_ij − Δ_i)))
   dQ_i  = round(scale·Σ_j dS_ij k_j),  dK_j = round(scale·Σ_i dS_ij q_i)
+
+with W = P in the dQ kernel, and in the dK/dV kernel W = P at D = 64 but
+W = round(P), the weights as rounded for the dV product, at D = 128 (its waves
+pass them from the one that makes P to the one that makes dS in that form).
 
 Sums are taken in fp32 by numpy (pairwise order) and products of 16-bit values
 are exact in fp64 before their fp32 rounding; the kernels' own summation orders
@@ -116,12 +120,14 @@ def fwd_emulate_head(q, k, v, scale: float, causal: bool, dtype: str, rows=None,
     return {"o": o, "o32": o32.astype(np.float64), "lse": lse.astype(np.float64), "rescales": moved}
 
 
-def bwd_emulate_head(q, k, v, o, lse, do, scale: float, causal: bool, dtype: str, exact: bool = False):
+def bwd_emulate_head(q, k, v, o, lse, do, scale: float, causal: bool, dtype: str, exact: bool = False,
+                     dk_weights: str = "auto"):
     """One head: the gradients the kernels compute from the stored o, lse (fp64 arrays).
 
     q [Lq, D], k/v [Lk, D], o/do [Lq, D] hold 16-bit values; lse [Lq] fp32 values.
     Returns (dq, dk, dv) as fp64 arrays of the rounded 16-bit results (exact=True:
-    no rounding anywhere, fp64).
+    no rounding anywhere, fp64).  dk_weights: the weights dK's dS is formed from,
+    "rounded" or "fp32"; "auto" as the kernels do (rounded at D = 128, fp32 at 64).
     """
     ft = np.float64 if exact else np.float32
     rnd = (lambda x: np.asarray(x, dtype=np.float64)) if exact else \
@@ -136,9 +142,12 @@ def bwd_emulate_head(q, k, v, o, lse, do, scale: float, causal: bool, dtype: str
     if causal:
         P[np.arange(Lk)[None, :] > np.arange(Lq)[:, None] + (Lk - Lq)] = 0
     dP = (do @ v.T).astype(ft)
+    if dk_weights == "auto":
+        dk_weights = "rounded" if q.shape[1] == 128 else "fp32"
     dS = (P * (dP - delta[:, None]).astype(ft)).astype(ft)
     Pr, dSr = rnd(P), rnd(dS)
+    dSr_k = dSr if dk_weights == "fp32" else rnd((Pr.astype(ft) * (dP - delta[:, None]).astype(ft)).astype(ft))
     dv = rnd((Pr.T @ do).astype(ft))
     dq = rnd(((dSr @ k).astype(ft) * ft(scale)).astype(ft))
-    dk = rnd(((dSr.T @ q).astype(ft) * ft(scale)).astype(ft))
+    dk = rnd(((dSr_k.T @ q).astype(ft) * ft(scale)).astype(ft))
     return dq, dk, dv

@@ -11,9 +11,9 @@ with TOL = 1e-2 (bf16) / 2e-3 (fp16) and TOL_RMS = 6e-3 / 8e-4, plus an absolute
 then an fp32 rounding residue, ~1e-7 at unit-scale inputs).  Derivation: the
 kernels round P and dS to the input type as matrix-core operands and round the
 outputs; the CPU model of exactly those roundings in fp32 (numerics.emulate, with
-O and LSE from the modelled forward pass) gives at most 6.2e-3 / 1.2e-3 of the
-slab's max and 2.7e-3 / 3.6e-4 of its rms, at L = 300..1024, D = 64 and 128,
-causal and not (tests/test_numerics.py).  The bars are 1.6–2.3x those.
+O and LSE from the modelled forward pass) gives at most 5.5e-3 / 1.2e-3 of the
+slab's max and 3.1e-3 / 4.0e-4 of its rms, at L = 300..1024, D = 64 and 128,
+causal and not (tests/test_numerics.py).  The bars are 1.7–2.0x those.
 Outputs are pre-filled with NaN so that an unwritten element fails.
 """
 

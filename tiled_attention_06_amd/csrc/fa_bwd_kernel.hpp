@@ -22,7 +22,9 @@
 //   * fa_bwd_dkdv_kernel: one workgroup = 4 waves = 128 keys, each wave owns 32
 //     keys (K and V rows resident in VGPRs); per 64-row query tile S = Q·Kᵀ and
 //     dP = dO·Vᵀ on MFMA, P and dS in registers (one key per lane), then
-//     dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS with dOᵀ and Qᵀ read transposed from LDS.
+//     dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS with dOᵀ and Qᵀ read transposed from LDS;
+//     at D = 128 without dropout fa_bwd_dkdv2_kernel instead: 8 waves, two per
+//     32 keys, one making S, P and dV, the other dP, dS and dK.
 // Each tile reaches LDS through the buffer unit (buffer_load ... lds, no VGPR
 // staging) in the forward pass's two LDS images: a row image for operands read
 // row by row and a transposing image for operands read across rows.  Two
@@ -31,7 +33,8 @@
 // results are deterministic.
 //
 // Numerics: fp32 accumulation; P and dS are rounded to the input type as MFMA
-// operands; dQ and dK are scaled in fp32 before the final rounding.
+// operands (fa_bwd_dkdv2_kernel forms dK's dS from P as rounded); dQ and dK are
+// scaled in fp32 before the final rounding.
 
 #pragma once
 
@@ -635,6 +638,215 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   unsigned char* const stv = wave == 0 ? qt0 : wave == 1 ? qt1 : wave == 2 ? ot0 : ot1;
   stage_rows_out<D, DT>(dk, p.scale, stk, lane, dkrs, j0w, p.sl[T_DK]);
   stage_rows_out<D, DT>(dv, 1.0f, stv, lane, dvrs, j0w, p.sl[T_DV]);
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV with two waves per key block: 8 waves = 128 keys.  Waves w and w + 4
+// (one SIMD) share keys 32w .. 32w + 31 of the workgroup and split the four
+// products of each 64-row query tile: wave w makes S = Q·Kᵀ, the weights P and
+// dVᵀ += dOᵀ·P; wave w + 4 makes dP = dO·Vᵀ, dS = P(dP − Δ) and dKᵀ += Qᵀ·dS.
+// The weights pass from one to the other through LDS as the rounded matrix-core
+// operand of dV (16 bytes per lane and 16-row group), between the two joins of a
+// step.  Each wave keeps one key operand and one accumulator (K and dV, or V and
+// dK): half the registers of one wave doing all four products, so two waves fit
+// on a SIMD and one's VALU work runs beside the other's MFMAs.
+// ---------------------------------------------------------------------------
+// the middle of a step: this wave's LDS writes are done, then a bare barrier
+__device__ __forceinline__ void bwd_lds_join() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv2_kernel(BwdParams p) {
+  using G = Geo<D>;
+  constexpr int NW = 8, BKV = 128, BQ = 64, NB = D / 32, KS = D / 16;
+  constexpr int NBLK = G::NBLK, KBS = G::KBS, VBS = G::VBS, KT = G::KT, VT = G::VT;
+  // per stage: Q row image, Q transposing image, dO row image, dO transposing image
+  __shared__ __attribute__((aligned(16))) unsigned char qr0[KT], qr1[KT], qt0[VT], qt1[VT];
+  __shared__ __attribute__((aligned(16))) unsigned char or0[KT], or1[KT], ot0[VT], ot1[VT];
+  // per stage: LSE·log2(e) and Δ of the tile's 64 rows (a 1 KB copy each; the
+  // first 256 bytes are used)
+  __shared__ __attribute__((aligned(16))) float ls0[256], ls1[256], de0[256], de1[256];
+  // the tile's weights, per key block, 32-row half qb and 16-row group h: [block][2qb + h][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 xw[4][4][64];
+  static_assert(2 * (2 * KT + 2 * VT) + 4 * 1024 + 4 * 4 * 64 * 16 <= 163840, "one workgroup per CU");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3;          // key block
+  const bool mk = wave < NW / 2;    // makes S, P, dV (else dP, dS, dK); wave-uniform
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int bid = blockIdx.x;
+  const int item = p.xcd_remap ? (bid & 7) * (p.num_wg >> 3) + (bid >> 3) : bid;
+  const int bh = __builtin_amdgcn_readfirstlane(item / p.n_kt);
+  const int kt = __builtin_amdgcn_readfirstlane(item - bh * p.n_kt);  // causal: low tiles see most rows
+  const int Lq = p.Lq, Lk = p.Lk;
+  const int j0 = kt * BKV, j0w = j0 + 32 * kw;
+  const int off = CAUSAL ? p.kv_off : 0;
+
+  const char* const qslab = bwd_slab((const char*)p.q, p, T_Q, bh);
+  const char* const doslab = bwd_slab((const char*)p.dout, p, T_DO, bh);
+  const uint32_t end_q = bwd_end<D>(p, T_Q, Lq), end_do = bwd_end<D>(p, T_DO, Lq);
+
+  // query tiles that see any key of this workgroup: rows i >= j0 - off (causal)
+  const int n_q = (Lq + BQ - 1) / BQ;
+  const int t_b = CAUSAL ? max(0, j0 - off) / BQ : 0;
+
+  const BwdCopy<D, NW> cpq(wave, lane, p.sl[T_Q]), cpo(wave, lane, p.sl[T_DO]);
+  // row statistics of tile t: rows past the padded end read 0
+  auto copy_stats = [&](const float* base, int t, float* dst) {
+    const uint64_t a = (uint64_t)(uintptr_t)(base + (int64_t)bh * p.Lq4 + (int64_t)t * BQ);
+    const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p.Lq4 - t * BQ) * 4u)),
+                      (uint32_t)kBufferFlags};
+    dma16(rs, (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(dst)), (uint32_t)(16 * lane));
+  };
+  auto copies = [&](int t, int st) {
+    cpq.template copy<KBS>(qslab, end_q, t, st ? qr1 : qr0);
+    cpq.template copy<VBS>(qslab, end_q, t, st ? qt1 : qt0);
+    cpo.template copy<KBS>(doslab, end_do, t, st ? or1 : or0);
+    cpo.template copy<VBS>(doslab, end_do, t, st ? ot1 : ot0);
+    if (wave == 0) copy_stats(p.ws_lse2, t, st ? ls1 : ls0);
+    if (wave == 1) copy_stats(p.ws_delta, t, st ? de1 : de0);
+  };
+  if (t_b < n_q) copies(t_b, 0);
+
+  // this wave's key rows as B operands (column = key l%32; slots of half g = head
+  // dims 16s+8g .. +7): K for S, or V for dP; keys past Lk read 0
+  const int key = j0w + l32;
+  const int T_B = mk ? T_K : T_V;
+  const auto brs = make_rsrc(bwd_slab((const char*)(mk ? p.k : p.v), p, T_B, bh), bwd_end<D>(p, T_B, Lk));
+  u32x4 br[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) br[s] = buf_load16(brs, (uint32_t)(key * p.sl[T_B] + 16 * s + 8 * g) * 2);
+  const float c = p.c;
+
+  auto row_off = [](int rows, int BS) { return (rows % NBLK) * BS + (rows / NBLK) * 2 * D; };
+  const int k_off = (l32 % NBLK) * KBS + (l32 / NBLK) * 2 * D + 16 * g;
+  const int gi = lane >> 4, li = lane & 15;
+  const int t_off = (4 * (gi >> 1) + (li >> 2)) * VBS + 2 * (16 * (gi & 1) + 4 * (li & 3));
+
+  // dV (waves that make the weights) or dK (the others)
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+
+  // S (or dP) of both 32-row halves of a tile: the lane holds key l%32 and rows
+  // 32qb + 8(r/4) + 4g + r%4 of the tile (rows from the row image `rb`)
+  auto products = [&](const unsigned char* rb, f32x16 (&X)[2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      X[qb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) X[qb] = mfma32<DT>(lds_read16(rb + k_off + row_off(32 * qb, KBS) + 32 * s), br[s], X[qb]);
+    }
+  };
+  // acc[nb] += Aᵀ·B over the tile's 64 rows: A from the transposing image `tb`
+  // (dims block nb, rows 32qb + 16h .. +15), B = x[qb][h] (this lane's key, those rows)
+  auto grads = [&](const unsigned char* tb, const u32x4 (&x)[2][2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const unsigned char* a = tb + t_off + 64 * nb;
+          const u32x2 lo = lds_read_tr(a + row_off(32 * qb + 16 * h, VBS));
+          const u32x2 hi = lds_read_tr(a + row_off(32 * qb + 16 * h + 8, VBS));
+          acc[nb] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, x[qb][h], acc[nb]);
+        }
+  };
+  // the weights P = 2^(S·c − LSE₂) of the tile, packed (registers r = 8h + 2e + u of
+  // half qb: x[qb][h][e]); MASK: causal, keys right of a row's diagonal get 0
+  auto weights = [&](auto MASK, int i0, const f32x16 (&S)[2], const float* lsb, u32x4 (&x)[2][2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x4 ls[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) ls[a] = *(const f32x4*)(lsb + 32 * qb + 8 * a + 4 * g);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pr[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * h + 2 * e + u;
+            pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][r], c, -ls[r >> 2][r & 3]));
+            if constexpr (decltype(MASK)::value) {
+              const int row = i0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+              pr[u] = key > row + off ? 0.f : pr[u];
+            }
+          }
+          x[qb][h][e] = pack2<DT>(pr[0], pr[1]);
+        }
+        xw[kw][2 * qb + h][lane] = x[qb][h];
+      }
+    }
+  };
+  // dS = P(dP − Δ) of the tile from the weights as rounded, packed like the weights
+  auto dscores = [&](const f32x16 (&dP)[2], const float* deb, u32x4 (&x)[2][2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x4 de[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) de[a] = *(const f32x4*)(deb + 32 * qb + 8 * a + 4 * g);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 pw = xw[kw][2 * qb + h][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 pr = unpack2<DT>(pw[e]);
+          const int r = 8 * h + 2 * e;
+          x[qb][h][e] = pack2<DT>(pr.x * (dP[qb][r] - de[r >> 2][r & 3]),
+                                  pr.y * (dP[qb][r + 1] - de[(r + 1) >> 2][(r + 1) & 3]));
+        }
+      }
+    }
+  };
+
+  bwd_wait_join();
+  for (int t = t_b; t < n_q; ++t) {
+    const int st = (t - t_b) & 1;
+    if (t + 1 < n_q) copies(t + 1, st ^ 1);
+    const int i0 = t * BQ;
+    // Every key block takes every tile from the first one that any of the
+    // workgroup's keys sees: a block that no row of the tile sees gets all-zero
+    // weights from the mask, which adds nothing (skipping it made the compiler
+    // copy the accumulators between registers on every step).  One code path for
+    // both roles, which differ in the operands and the VALU step, for the same
+    // reason.
+    f32x16 X[2];
+    products(mk ? (st ? qr1 : qr0) : (st ? or1 : or0), X);  // S, or dP
+    u32x4 x[2][2];
+    if (mk) {
+      // causal: only tiles that reach right of some row's diagonal are masked
+      if (CAUSAL && j0w + 31 > i0 + off)
+        weights(std::true_type{}, i0, X, st ? ls1 : ls0, x);
+      else
+        weights(std::false_type{}, i0, X, st ? ls1 : ls0, x);
+    }
+    bwd_lds_join();
+    if (!mk) dscores(X, st ? de1 : de0, x);
+    grads(mk ? (st ? ot1 : ot0) : (st ? qt1 : qt0), x);  // dVᵀ += dOᵀ·P, or dKᵀ += Qᵀ·dS
+    bwd_wait_join();
+  }
+
+  // epilogue: lane holds dims 32nb + 8(r/4) + 4g + r%4 of key `key`; each wave's
+  // 32 rows of dV or dK go row-major through its own LDS buffer (free since the
+  // last barrier) and out as whole rows (see stage_rows_out)
+  static_assert(32 * (2 * D + 16) <= KT, "staging fits");
+  unsigned char* const stg = wave == 0 ? qt0 : wave == 1 ? qt1 : wave == 2 ? ot0 : wave == 3 ? ot1
+                           : wave == 4 ? qr0 : wave == 5 ? qr1 : wave == 6 ? or0 : or1;
+  const int T_G = mk ? T_DV : T_DK;
+  const auto grs = make_rsrc(bwd_slab((char*)(mk ? p.dv : p.dk), p, T_G, bh), bwd_end<D>(p, T_G, Lk));
+  stage_rows_out<D, DT>(acc, mk ? 1.0f : p.scale, stg, lane, grs, j0w, p.sl[T_G]);
 }
 
 }  // namespace fa355
