@@ -31,6 +31,7 @@ CASES = [  # B, H, Lq, Lk, D, dtype, causal, p, seed
     (1, 2, 100, 1000, 128, "fp16", True, 0.3, 77),
     (1, 1, 1, 777, 64, "bf16", False, 0.9, 5),
     (1, 2, 520, 520, 64, "bf16", True, 0.25, 99),
+    (2, 2, 333, 270, 128, "bf16", False, 0.2, 4242),
 ]
 IDS = [f"B{b}H{h}_{lq}x{lk}_D{d}_{dt}_{'c' if c else 'nc'}_p{p}" for b, h, lq, lk, d, dt, c, p, _ in CASES]
 

@@ -305,14 +305,13 @@ int launch_bwd(fa355::BwdParams p, hipStream_t stream) {
   if (st != FA_OK) return st;
   p.num_wg = p.bh * p.n_kt;
   p.xcd_remap = (p.num_wg % 8 == 0) ? 1 : 0;
-  // D = 128 without dropout: two waves per key block (measured 10% faster per
-  // backward call at the 7B 4K shape); otherwise one wave doing all four products
-  // (at D = 64 half the matrix work per step does not pay for the split's second
-  // join: 10% slower there)
-  if constexpr (DROP || D == 64)
+  // D = 128: two waves per key block (measured 10% faster per backward call at
+  // the 7B 4K shape); D = 64: one wave doing all four products (half the matrix
+  // work per step does not pay for the split's second join: 10% slower there)
+  if constexpr (D == 64)
     hipLaunchKernelGGL((fa355::fa_bwd_dkdv_kernel<D, DT, CAUSAL, DROP>), dim3(p.num_wg), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((fa355::fa_bwd_dkdv2_kernel<D, DT, CAUSAL>), dim3(p.num_wg), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fa355::fa_bwd_dkdv2_kernel<D, DT, CAUSAL, DROP>), dim3(p.num_wg), dim3(512), 0, stream, p);
   return launch_status();
 }
 

@@ -659,7 +659,7 @@ __device__ __forceinline__ void bwd_lds_join() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv2_kernel(BwdParams p) {
   using G = Geo<D>;
   constexpr int NW = 8, BKV = 128, BQ = 64, NB = D / 32, KS = D / 16;
@@ -762,19 +762,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           acc[nb] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, x[qb][h], acc[nb]);
         }
   };
-  // the weights P = 2^(S·c − LSE₂) of the tile, packed (registers r = 8h + 2e + u of
-  // half qb: x[qb][h][e]); MASK: causal, keys right of a row's diagonal get 0
+  // Dropout words of half qb for this lane's key: block x = 2h + a covers rows
+  // i0 + 32qb + 16h + 8a + 4g + 0..3.  The four lanes of a quad share the key block,
+  // so lane j computes block j and the quad exchanges them through LDS (in this key
+  // block's weight buffer, slot 2qb, which the weights of the half overwrite after).
+  auto drop_half = [&](int qb, int i0, u32x4 (&blk)[4]) {
+    const int j = lane & 3, h = j >> 1, a = j & 1;
+    const u32x4 mine = drop_block(key >> 2, (i0 + 32 * qb + 16 * h + 8 * a + 4 * g) >> 2, bh, p.seed_lo, p.seed_hi);
+    u32x4* const xb = &xw[kw][2 * qb][0] + 4 * (lane >> 2);
+    xb[j] = mine;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) blk[x] = xb[x];
+  };
+  // the weights P = 2^(S·c − LSE₂) of the tile, packed as the B operand of dV
+  // (registers r = 8h + 2e + u of half qb: x[qb][h][e]); MASK: causal, keys right of
+  // a row's diagonal get 0.  The other wave of the key block gets them in the same
+  // form; with dropout x holds the kept weights times 1/(1 − p), and the other wave
+  // gets the weights before dropout with the sign bit of each dropped one set.
   auto weights = [&](auto MASK, int i0, const f32x16 (&S)[2], const float* lsb, u32x4 (&x)[2][2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x4 ls[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) ls[a] = *(const f32x4*)(lsb + 32 * qb + 8 * a + 4 * g);
+      u32x4 blk[4];
+      if constexpr (DROP) drop_half(qb, i0, blk);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        u32x4 xo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float pr[2];
+          bool kept[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int r = 8 * h + 2 * e + u;
@@ -783,14 +802,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const int row = i0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
               pr[u] = key > row + off ? 0.f : pr[u];
             }
+            if constexpr (DROP) kept[u] = ((blk[2 * h + (e >> 1)][2 * (e & 1) + u] >> (8 * (key & 3))) & 0xffu) < p.drop_t;
           }
-          x[qb][h][e] = pack2<DT>(pr[0], pr[1]);
+          if constexpr (DROP) {
+            x[qb][h][e] = pack2<DT>(kept[0] ? pr[0] * p.drop_scale : 0.f, kept[1] ? pr[1] * p.drop_scale : 0.f);
+            xo[e] = pack2<DT>(pr[0], pr[1]) | (kept[0] ? 0u : 0x8000u) | (kept[1] ? 0u : 0x80000000u);
+          } else {
+            x[qb][h][e] = pack2<DT>(pr[0], pr[1]);
+          }
         }
-        xw[kw][2 * qb + h][lane] = x[qb][h];
+        xw[kw][2 * qb + h][lane] = DROP ? xo : x[qb][h];
       }
     }
   };
   // dS = P(dP − Δ) of the tile from the weights as rounded, packed like the weights
+  // (with dropout dS = P(dP·m − Δ), m the kept weight's scale or 0)
   auto dscores = [&](const f32x16 (&dP)[2], const float* deb, u32x4 (&x)[2][2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -802,10 +828,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const u32x4 pw = xw[kw][2 * qb + h][lane];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float2 pr = unpack2<DT>(pw[e]);
           const int r = 8 * h + 2 * e;
-          x[qb][h][e] = pack2<DT>(pr.x * (dP[qb][r] - de[r >> 2][r & 3]),
-                                  pr.y * (dP[qb][r + 1] - de[(r + 1) >> 2][(r + 1) & 3]));
+          float dp0 = dP[qb][r], dp1 = dP[qb][r + 1];
+          uint32_t w = pw[e];
+          if constexpr (DROP) {
+            dp0 *= (w & 0x8000u) ? 0.f : p.drop_scale;
+            dp1 *= (w & 0x80000000u) ? 0.f : p.drop_scale;
+            w &= 0x7fff7fffu;
+          }
+          const float2 pr = unpack2<DT>(w);
+          x[qb][h][e] = pack2<DT>(pr.x * (dp0 - de[r >> 2][r & 3]), pr.y * (dp1 - de[(r + 1) >> 2][(r + 1) & 3]));
         }
       }
     }
