@@ -318,7 +318,7 @@ def summarize_traffic(directory: str, w, pass_: str = "fwd") -> str:
     per = {}
     for r in rows:
         per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
-    ours = ("fa_fwd_kernel",) if pass_ == "fwd" else ("fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel")
+    ours = ("fa_fwd_kernel",) if pass_ == "fwd" else ("fa_bwd_dq_kernel", "fa_bwd_dkdv")  # dkdv2 at D = 128
     mine = {name: [c for (kn, _), c in per.items() if name in kn] for name in ours}
     if not all(mine.values()):
         raise SystemExit(f"no dispatches of {[n for n, c in mine.items() if not c]} in the counter CSVs")
@@ -747,7 +747,7 @@ def bench_bwd(args, w) -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
                      "traffic": committed_traffic(w.name, "bwd") if not args.dropout else None,
-                     "kernel": "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (the events bracket both)", "mean_launch_us": round(mean_s * 1e6, 3)},
+                     "kernel": "fa_bwd_dq_kernel + fa_bwd_dkdv2_kernel (fa_bwd_dkdv_kernel at D = 64; the events bracket both)", "mean_launch_us": round(mean_s * 1e6, 3)},
         "timing": res["timing"],
     }
     at_clock(out["timing"], achieved)
