@@ -242,8 +242,7 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   p.bh = (int)((int64_t)B * H);
   p.ws_o = splits > 1 ? (float*)ws : nullptr;
   p.ws_ml = splits > 1 ? (float*)((char*)ws + ws_o_bytes(B, H, Lq, D, splits)) : nullptr;
-  p.xcd_remap = (n_rep == 2 ? ((int64_t)B * H * n_qt) % 16 == 0 : num_wg % 8 == 0) ? 1 : 0;
-  p.n_rep = n_rep;
+  p.wg_order = ((n_rep == 2 ? ((int64_t)B * H * n_qt) % 16 == 0 : num_wg % 8 == 0) ? 1 : 0) | (n_rep == 2 ? 2 : 0);
   // The softmax runs in base 2 with the scale folded into one positive factor;
   // a negative scale negates Q (exact in fp16/bf16) and a zero scale zeroes it.
   const double log2e = 1.4426950408889634074;

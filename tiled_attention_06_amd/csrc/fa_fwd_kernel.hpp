@@ -104,8 +104,8 @@ struct FwdParams {
   int bh;           // B * H
   float* ws_o;      // n_split > 1: unnormalised partial outputs, fp32 [n_split][B*H][Lq][D]
   float* ws_ml;     // n_split > 1: per row (m, l_f, l_r, 0), fp32 [n_split][B*H][Lq][4]
-  int xcd_remap;    // 1: group consecutive work items on one XCD
-  int n_rep;        // work items per workgroup: 1, or 2 (paired form, two key groups only)
+  int wg_order;     // bit 0: group consecutive work items on one XCD; bit 1: two
+                    // work items per workgroup (paired form, two key groups only)
   float c;          // |scale| * log2(e), or log2(e) when scale == 0 (always > 0)
   uint32_t q_and;   // 0xffffffff, or 0 when scale == 0 (Q forced to zero)
   uint32_t q_xor;   // 0x80008000 when scale < 0 (Q negated exactly), else 0
@@ -368,11 +368,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // without dropout; the dropout kernels have no scalar registers to spare for
   // the loop.
   constexpr bool PAIRABLE = KG == 2 && !DROP;
-  const int n_rep = PAIRABLE ? args.n_rep : 1;
+  const int n_rep = PAIRABLE ? 1 + ((args.wg_order >> 1) & 1) : 1;
   // Q rows of the current item as loaded (the sign / zero transform of the scale
   // is applied once they are in)
   u32x4 qr[G::KS];
-  for (int rep = 0; rep < n_rep; ++rep) {
+  // One work item (the rep-th of this workgroup); false: there is none.  A lambda
+  // called once outside the paired form, so that those kernels compile as a plain
+  // body (with a loop around it their register allocation and schedule shifted:
+  // the dropout kernel lost 9%).
+  auto item_body = [&](int rep) -> bool {
   const FwdParams p = PAIRABLE ? reread_args<FwdParams>() : args;
   // Item r of this workgroup: batch*head, query tile counted from the heaviest,
   // key split; false if there is none.  Paired form (n_rep == 2): the items of an
@@ -382,12 +386,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto locate = [&](const FwdParams& pa, int r, int& bh_, int& qtr_, int& split_) -> bool {
     int item_s;
     if (PAIRABLE && n_rep == 2) {
-      const int nb = pa.xcd_remap ? 8 : 1;
+      const int nb = (pa.wg_order & 1) ? 8 : 1;
       const int x = bid % nb, i = bid / nb, mi = pa.bh * pa.n_qt / nb;
       if (r && mi - 1 - i == i) return false;  // the middle item of an odd block runs once
       item_s = x * mi + (r ? mi - 1 - i : i);
     } else {
-      item_s = pa.xcd_remap ? (bid & 7) * (pa.num_wg >> 3) + (bid >> 3) : bid;
+      item_s = (pa.wg_order & 1) ? (bid & 7) * (pa.num_wg >> 3) + (bid >> 3) : bid;
     }
     // the key splits of one (batch*head, query tile) are consecutive items
     const int item = item_s / pa.n_split;
@@ -413,12 +417,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     return true;
   };
   int bh, qt_r, split;
-  if (!locate(p, rep, bh, qt_r, split)) break;
-  // thread-derived values taken afresh for each item (see opaque()): derived once
-  // before the loop, they and what the compiler computes from them would stay
-  // live across all of it
-  const int lane = opaque(tid) & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(opaque(tid) >> 6);
+  if (!locate(p, rep, bh, qt_r, split)) return false;
+  // in the paired form thread-derived values are taken afresh for each item (see
+  // opaque()): derived once before the loop, they and what the compiler computes
+  // from them would stay live across all of it
+  const int tid_i = PAIRABLE ? opaque(tid) : tid;
+  const int lane = tid_i & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid_i >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int qt = CAUSAL ? p.n_qt - 1 - qt_r : qt_r;
   const int i0 = qt * G::BR;
@@ -930,7 +935,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (te2 > 1) copy_tile(kslab2, tb_k, end_k, step_k, src_k, ks1, 1, KBSc);
       }
     }
-    if (kg == 1) continue;
+    if (kg == 1) return true;
     if (live) {
       const float m1 = xst[wr][0][lane];
       const float mm = fmaxf(m_run, m1);
@@ -973,7 +978,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const u32x4 st = {__float_as_uint(m_run), __float_as_uint(lf_t), __float_as_uint(lr_t), 0u};
       *(u32x4*)(p.ws_ml + (part * Lq + row_e) * 4) = st;
     }
-    continue;
+    return true;
   }
   // one pass: normalise by the sum of the rounded weights, store O and LSE.  The
   // accumulator layout gives a lane 4 dims of one row per 8 bytes, scattered over
@@ -1009,6 +1014,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     buf_store16(ors, (uint32_t)((i0w + r) * o_sl + ch * 8) * 2, x);  // rows >= Lq are dropped
   }
   if (g_e == 0 && row_e < Lq) p.lse[(size_t)bh * Lq + row_e] = (m_run + log2f(lf_t)) * 0.69314718055994530942f;
+  return true;
+  };
+  if constexpr (PAIRABLE) {
+    for (int rep = 0; rep < n_rep; ++rep)
+      if (!item_body(rep)) break;
+  } else {
+    item_body(0);
   }
 }
 
