@@ -75,6 +75,7 @@ CASES = [  # B, H, Lq, Lk, D, dtype, causal
     (1, 2, 100, 1000, 128, "fp16", True), (1, 2, 1000, 100, 64, "bf16", False), (1, 1, 1, 1, 128, "bf16", False),
     (1, 1, 1, 1, 64, "fp16", True), (1, 2, 129, 65, 128, "fp16", False), (1, 1, 513, 513, 128, "bf16", True),
     (1, 2, 200, 333, 64, "bf16", True), (1, 1, 640, 640, 128, "fp16", False),
+    (2, 2, 200, 333, 128, "bf16", True), (1, 3, 70, 130, 128, "fp16", True),
 ]
 
 
