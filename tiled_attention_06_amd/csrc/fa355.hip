@@ -85,7 +85,8 @@ int dispatch_dtype(const fa355::FwdParams& p, const fa355::MergeParams& m, int d
   if (dtype == FA_DTYPE_BF16)
     return causal ? launch<D, fa355::DT_BF16, true, DROP, KG>(p, m, s)
                   : launch<D, fa355::DT_BF16, false, DROP, KG>(p, m, s);
-  return causal ? launch<D, fa355::DT_F16, true, DROP, KG>(p, m, s) : launch<D, fa355::DT_F16, false, DROP, KG>(p, m, s);
+  return causal ? launch<D, fa355::DT_F16, true, DROP, KG>(p, m, s)
+                : launch<D, fa355::DT_F16, false, DROP, KG>(p, m, s);
 }
 
 // Compute units of the current device (0 if it cannot be read), cached per thread and device.
@@ -393,8 +394,10 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
   p.drop_scale = (float)(256.0 / drop_t);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (drop_t < 256)
-    return D == 128 ? dispatch_bwd<128, true>(p, dtype, causal != 0, s) : dispatch_bwd<64, true>(p, dtype, causal != 0, s);
-  return D == 128 ? dispatch_bwd<128, false>(p, dtype, causal != 0, s) : dispatch_bwd<64, false>(p, dtype, causal != 0, s);
+    return D == 128 ? dispatch_bwd<128, true>(p, dtype, causal != 0, s)
+                    : dispatch_bwd<64, true>(p, dtype, causal != 0, s);
+  return D == 128 ? dispatch_bwd<128, false>(p, dtype, causal != 0, s)
+                  : dispatch_bwd<64, false>(p, dtype, causal != 0, s);
 }
 
 }  // namespace

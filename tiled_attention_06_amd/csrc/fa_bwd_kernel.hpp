@@ -744,7 +744,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int qb = 0; qb < 2; ++qb) {
       X[qb] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) X[qb] = mfma32<DT>(lds_read16(rb + k_off + row_off(32 * qb, KBS) + 32 * s), br[s], X[qb]);
+      for (int s = 0; s < KS; ++s)
+        X[qb] = mfma32<DT>(lds_read16(rb + k_off + row_off(32 * qb, KBS) + 32 * s), br[s], X[qb]);
     }
   };
   // acc[nb] += Aᵀ·B over the tile's 64 rows: A from the transposing image `tb`
@@ -802,7 +803,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const int row = i0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
               pr[u] = key > row + off ? 0.f : pr[u];
             }
-            if constexpr (DROP) kept[u] = ((blk[2 * h + (e >> 1)][2 * (e & 1) + u] >> (8 * (key & 3))) & 0xffu) < p.drop_t;
+            if constexpr (DROP)
+              kept[u] = ((blk[2 * h + (e >> 1)][2 * (e & 1) + u] >> (8 * (key & 3))) & 0xffu) < p.drop_t;
           }
           if constexpr (DROP) {
             x[qb][h][e] = pack2<DT>(kept[0] ? pr[0] * p.drop_scale : 0.f, kept[1] ? pr[1] * p.drop_scale : 0.f);
