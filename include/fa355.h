@@ -222,7 +222,7 @@ int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
  * also writes every row's D_i and lse_i*log2(e) to the workspace, then dk and
  * dv, which read them); the call returns without synchronising.
  * Precision: fp32 accumulation; P and dS are rounded to `dtype` as matrix-core
- * operands.  Each output element is written by exactly one thread, in a fixed
+ * operands (at D = 128 dk's dS is formed from P as rounded).  Each output element is written by exactly one thread, in a fixed
  * order, so results are bitwise reproducible.
  */
 size_t fa_bwd_workspace_size(int B, int H, int Lq);
@@ -292,6 +292,32 @@ int fa_last_hip_error(void);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int fa_version(void);
+
+/*
+ * fa_fwd_launch_shape — the grid of the attention kernel that fa_fwd
+ * (fa_fwd_strided, fa_fwd_dropout with num_splits = 1, fa_fwd_splitkv with
+ * num_splits) launches for these sizes on the calling thread's current device:
+ * for callers that plan around it, and for tests of the launch forms.  No device
+ * memory is touched and nothing is enqueued; the device's CU count is read once.
+ *
+ *   workgroups           workgroups of the attention kernel (written)
+ *   rows_per_workgroup   query rows of one work item (written): 256, or 128 in
+ *                        the two-key-group form, taken by a single pass whose
+ *                        grid of 256-row items would not exceed the CU count
+ *   items_per_workgroup  1, or 2 in the paired form (written): two-key-group
+ *                        grids without dropout whose items outnumber the CUs
+ *                        (causal ones only when each XCD's block of items holds
+ *                        whole pairs of heads); a workgroup then runs a heavy
+ *                        and a light causal query block
+ *
+ * Returns FA_OK, or the status fa_fwd would return for these sizes:
+ * FA_ERR_NULL (an output pointer is NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM,
+ * FA_ERR_CAUSAL_SHAPE, FA_ERR_DROPOUT, FA_ERR_SPLITS (num_splits outside
+ * 1..256, or above 1 with dropout).  When the CU count cannot be read the
+ * 256-row form is reported, as the forward call would then launch it.
+ */
+int fa_fwd_launch_shape(int B, int H, int Lq, int Lk, int D, int causal, float dropout_p, int num_splits,
+                        int* workgroups, int* rows_per_workgroup, int* items_per_workgroup);
 
 #ifdef __cplusplus
 }

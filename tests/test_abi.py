@@ -51,7 +51,7 @@ def test_header_declares_the_abi():
     assert declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
                                     "fa_fwd_splitkv_noalloc", "fa_bwd_workspace_size", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout",
                                     "fa_fwd_dropout_strided", "fa_bwd_strided", "fa_status_string",
-                                    "fa_last_hip_error", "fa_version"]
+                                    "fa_last_hip_error", "fa_version", "fa_fwd_launch_shape"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -420,3 +420,31 @@ def test_bwd_strided_checks():
         big[3 * t + 2] = 28_823_037_615_171_176
         assert call_bwd_strided(strides=big) == -2
     assert call_bwd_strided(p=1.0) == -13
+
+
+def test_launch_shape_query():
+    # fa_fwd_launch_shape: argument statuses as fa_fwd's, checked before any device query; for valid sizes a
+    # grid that covers every query row once (256-row items, or 128-row items one or two to a workgroup)
+    ref = (ctypes.c_int(), ctypes.c_int(), ctypes.c_int())
+    out = [ctypes.byref(x) for x in ref]
+    q = fa.lib.fa_fwd_launch_shape
+    assert q(1, 1, 64, 64, 128, 0, 0.0, 1, None, out[1], out[2]) == -1
+    assert q(0, 1, 64, 64, 128, 0, 0.0, 1, *out) == -2
+    assert q(1, 1, 64, 64, 96, 0, 0.0, 1, *out) == -3
+    assert q(1, 1, 65, 64, 128, 1, 0.0, 1, *out) == -7
+    assert q(1, 1, 64, 64, 128, 0, 0.0, 0, *out) == -11
+    assert q(1, 1, 64, 64, 128, 0, 0.0, 257, *out) == -11
+    assert q(1, 1, 64, 64, 128, 0, 0.1, 2, *out) == -11
+    assert q(1, 1, 64, 64, 128, 0, 1.5, 1, *out) == -13
+    for B, H, Lq, Lk, D, causal, p, splits in [(4, 32, 4096, 4096, 128, True, 0.0, 1), (1, 32, 2048, 2048, 128, True, 0.0, 1),
+                                              (1, 19, 1900, 1900, 64, False, 0.0, 1), (1, 8, 1, 32768, 128, True, 0.0, 32),
+                                              (2, 3, 300, 300, 128, True, 0.2, 1)]:
+        wg, rows, items = fa.fa_fwd_launch_shape(B, H, Lq, Lk, D, causal, p, splits)
+        assert rows in (128, 256) and items in (1, 2)
+        n_items = B * H * -(-Lq // rows)
+        if rows == 256:
+            assert items == 1 and wg == n_items * splits
+        else:
+            assert splits == 1 and wg == -(-n_items // items)
+        if p > 0:
+            assert items == 1

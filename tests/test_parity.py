@@ -204,6 +204,11 @@ def test_paired_form(H, L, D, dtype, causal):
     inp = ai.make_custom(1, H, L, L, D, dtype, causal, seed=37_000 + H)
     note(f"paired form B1 H{H} L{L} D{D} {dtype} causal={causal}")
     n = H // 2
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        # the full grid runs paired, the subset one item per workgroup (both in 128-row items)
+        n_items = H * -(-L // 128)
+        assert fa.fa_fwd_launch_shape(1, H, L, L, D, causal) == ((n_items + 1) // 2, 128, 2)
+        assert fa.fa_fwd_launch_shape(1, n, L, L, D, causal) == (n * -(-L // 128), 128, 1)
     sub = {**inp, **{x: inp[x][:, :n].contiguous() for x in ("q", "k", "v")}}
     o_all, l_all = run_gpu(inp)
     o_sub, l_sub = run_gpu(sub)

@@ -9,7 +9,8 @@ Names follow the C ABI: ``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_status_string``, ``fa_last_hip_error``,
 ``fa_version``, ``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_fwd_dropout``,
 ``fa_bwd_dropout``, ``fa_fwd_dropout_strided``, ``fa_bwd_strided`` (reached through ``fa_fwd`` /
-``fa_bwd`` with views and ``dropout_p``), ``fa_fwd_splitkv_noalloc``; ``fa_fwd_qkvpacked`` is a
+``fa_bwd`` with views and ``dropout_p``), ``fa_fwd_splitkv_noalloc``, ``fa_fwd_launch_shape``;
+``fa_fwd_qkvpacked`` is a
 view helper over ``fa_fwd_strided`` for a packed [B, L, 3, H, D] qkv buffer,
 ``suggest_num_splits`` a host heuristic, and ``flash_attention`` an autograd
 function whose forward is ``fa_fwd`` and whose backward is ``fa_bwd``.
@@ -27,7 +28,7 @@ __all__ = ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_workspa
            "fa_fwd_splitkv_noalloc", "FA_NOALLOC_SCRATCH_BYTES",
            "suggest_num_splits", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout",
            "flash_attention", "fa_status_string",
-           "fa_last_hip_error", "fa_version", "FaError", "lib", "LIB_PATH", "FA_DTYPE_F16", "FA_DTYPE_BF16"]
+           "fa_last_hip_error", "fa_version", "fa_fwd_launch_shape", "FaError", "lib", "LIB_PATH", "FA_DTYPE_F16", "FA_DTYPE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
 
@@ -76,6 +77,9 @@ def _load() -> ctypes.CDLL:
     lib.fa_last_hip_error.restype = i
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i
+    lib.fa_fwd_launch_shape.argtypes = [i, i, i, i, i, i, ctypes.c_float, i, ctypes.POINTER(i), ctypes.POINTER(i),
+                                        ctypes.POINTER(i)]
+    lib.fa_fwd_launch_shape.restype = i
     return lib
 
 
@@ -255,6 +259,18 @@ def fa_fwd_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o:
     if code != 0:
         raise FaError(code)
     return o, lse
+
+
+def fa_fwd_launch_shape(B: int, H: int, Lq: int, Lk: int, D: int, causal: bool, dropout_p: float = 0.0,
+                        num_splits: int = 1) -> tuple[int, int, int]:
+    """(workgroups, rows per work item, work items per workgroup) of the forward kernel for these sizes on the
+    current device (``fa_fwd_launch_shape``)."""
+    wg, rows, items = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    code = lib.fa_fwd_launch_shape(B, H, Lq, Lk, D, int(bool(causal)), float(dropout_p), num_splits,
+                                   ctypes.byref(wg), ctypes.byref(rows), ctypes.byref(items))
+    if code != 0:
+        raise FaError(code)
+    return wg.value, rows.value, items.value
 
 
 def suggest_num_splits(B: int, H: int, Lq: int, Lk: int, D: int, causal: bool, num_cu: int = 256) -> int:

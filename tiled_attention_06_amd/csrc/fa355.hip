@@ -151,6 +151,47 @@ size_t ws_bytes(int B, int H, int Lq, int D, int splits) {
   return splits <= 1 ? 0 : ws_o_bytes(B, H, Lq, D, splits) + (size_t)splits * B * H * Lq * 4 * 4;
 }
 
+// The forward kernel's grid for valid sizes.  Workgroups of 8 waves and 256
+// rows; a single pass (no key splits) whose grid would not exceed the CU count
+// takes 128 rows per workgroup instead, with the 8 waves in two key groups that
+// take alternate key tiles: twice the workgroups, the heaviest causal ones half
+// as long, and still two waves per SIMD.  When those items outnumber the CUs (and
+// without dropout), each workgroup runs two of them, from both ends of its XCD's
+// block of items (the whole grid when the item count is no multiple of 16): a
+// heavy causal tile and then a light one, whose sum is the same for every
+// workgroup when a block holds whole pairs of heads (causal grids are paired only
+// then).  The second item's first loads overlap the first one's merge and stores,
+// and no workgroup is launched twice on a CU.
+struct FwdPlan {
+  int64_t n_qt;     // query tiles per head
+  bool narrow;      // 128-row two-key-group form
+  int n_rep;        // items per workgroup
+  int64_t num_wg;   // workgroups
+  int wg_order;     // the kernel's order flags (FwdParams::wg_order)
+};
+FwdPlan plan_fwd(int B, int H, int Lq, int causal, int splits, int drop_t) {
+  static_assert(fa355::Geo<64>::BR == fa355::Geo<128>::BR && fa355::Geo<64, 8, 2>::BR == fa355::Geo<128, 8, 2>::BR,
+                "row tile independent of D");
+  FwdPlan pl;
+  pl.n_qt = ((int64_t)Lq + fa355::Geo<128>::BR - 1) / fa355::Geo<128>::BR;
+  pl.narrow = false;
+  pl.n_rep = 1;
+  if (splits == 1 && (int64_t)B * H * pl.n_qt <= 2048) {
+    const int cus = cu_count();
+    pl.narrow = cus > 0 && (int64_t)B * H * pl.n_qt <= cus;
+    if (pl.narrow) {
+      pl.n_qt = ((int64_t)Lq + fa355::Geo<128, 8, 2>::BR - 1) / fa355::Geo<128, 8, 2>::BR;
+      const int64_t n_items = (int64_t)B * H * pl.n_qt;
+      const int64_t per_block = n_items % 16 == 0 ? n_items / 8 : n_items;
+      if (drop_t >= 256 && n_items > cus && (!causal || per_block % (2 * pl.n_qt) == 0)) pl.n_rep = 2;
+    }
+  }
+  const int64_t n_items = (int64_t)B * H * pl.n_qt;
+  pl.num_wg = pl.n_rep == 2 ? (n_items + 1) / 2 : n_items * splits;
+  pl.wg_order = ((pl.n_rep == 2 ? n_items % 16 == 0 : pl.num_wg % 8 == 0) ? 1 : 0) | (pl.n_rep == 2 ? 2 : 0);
+  return pl;
+}
+
 int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk, int D,
         const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride, const int64_t* o_stride,
         float scale, int causal, int dtype, int splits, void* ws, size_t ws_size, fa_stream_t stream,
@@ -187,34 +228,9 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   for (int i = 0; i < 4; ++i)
     if (st[i][2] > ((1ll << 31) - 1 - D) / (lens[i] + 256)) return FA_ERR_SHAPE;
   if (splits > 1 && ((int64_t)Lq + 256) * D * 4 >= (1ll << 32)) return FA_ERR_SHAPE;  // one partial slab
-  // Workgroups of 8 waves and 256 rows; a single pass (no key splits) whose grid
-  // would not exceed the CU count takes 128 rows per workgroup instead, with the
-  // 8 waves in two key groups that take alternate key tiles: twice the
-  // workgroups, the heaviest causal ones half as long, and still two waves per
-  // SIMD.  When those items outnumber the CUs (and without dropout), each
-  // workgroup runs two of them, from both ends of its XCD's block of items (the
-  // whole grid when the item count is no multiple of 16): a heavy causal tile
-  // and then a light one, whose sum is the same for every workgroup when a block
-  // holds whole pairs of heads (causal grids are paired only then).  The second
-  // item's first loads overlap the first one's merge and stores, and no
-  // workgroup is launched twice on a CU.
-  const int BR8 = fa355::Geo<128>::BR;
-  static_assert(fa355::Geo<64>::BR == fa355::Geo<128>::BR && fa355::Geo<64, 8, 2>::BR == fa355::Geo<128, 8, 2>::BR,
-                "row tile independent of D");
-  int64_t n_qt = ((int64_t)Lq + BR8 - 1) / BR8;
-  bool narrow = false;
-  int n_rep = 1;
-  if (splits == 1 && (int64_t)B * H * n_qt <= 2048) {
-    const int cus = cu_count();
-    narrow = cus > 0 && (int64_t)B * H * n_qt <= cus;
-    if (narrow) {
-      n_qt = ((int64_t)Lq + fa355::Geo<128, 8, 2>::BR - 1) / fa355::Geo<128, 8, 2>::BR;
-      const int64_t n_items = (int64_t)B * H * n_qt;
-      const int64_t per_block = n_items % 16 == 0 ? n_items / 8 : n_items;
-      if (drop_t >= 256 && n_items > cus && (!causal || per_block % (2 * n_qt) == 0)) n_rep = 2;
-    }
-  }
-  const int64_t num_wg = n_rep == 2 ? ((int64_t)B * H * n_qt + 1) / 2 : (int64_t)B * H * n_qt * splits;
+  const FwdPlan pl = plan_fwd(B, H, Lq, causal, splits, drop_t);
+  const int64_t n_qt = pl.n_qt, num_wg = pl.num_wg;
+  const bool narrow = pl.narrow;
   if ((int64_t)B * H >= (1ll << 31) || num_wg >= (1ll << 22)) return FA_ERR_SHAPE;
 
   if (splits > 1 && use_scratch) {  // every argument is valid: now the one HIP query
@@ -243,7 +259,7 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   p.bh = (int)((int64_t)B * H);
   p.ws_o = splits > 1 ? (float*)ws : nullptr;
   p.ws_ml = splits > 1 ? (float*)((char*)ws + ws_o_bytes(B, H, Lq, D, splits)) : nullptr;
-  p.wg_order = ((n_rep == 2 ? ((int64_t)B * H * n_qt) % 16 == 0 : num_wg % 8 == 0) ? 1 : 0) | (n_rep == 2 ? 2 : 0);
+  p.wg_order = pl.wg_order;
   // The softmax runs in base 2 with the scale folded into one positive factor;
   // a negative scale negates Q (exact in fp16/bf16) and a zero scale zeroes it.
   const double log2e = 1.4426950408889634074;
@@ -510,5 +526,22 @@ const char* fa_status_string(int status) {
 int fa_last_hip_error(void) { return g_last_hip_error; }
 
 int fa_version(void) { return kVersion; }
+
+int fa_fwd_launch_shape(int B, int H, int Lq, int Lk, int D, int causal, float dropout_p, int num_splits,
+                        int* workgroups, int* rows_per_workgroup, int* items_per_workgroup) {
+  if (!workgroups || !rows_per_workgroup || !items_per_workgroup) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (causal && Lq > Lk) return FA_ERR_CAUSAL_SHAPE;
+  const int drop_t = drop_threshold(dropout_p);
+  if (drop_t < 0) return FA_ERR_DROPOUT;
+  if (num_splits < 1 || num_splits > kMaxSplits || (drop_t < 256 && num_splits > 1)) return FA_ERR_SPLITS;
+  const FwdPlan pl = plan_fwd(B, H, Lq, causal, num_splits, drop_t);
+  if ((int64_t)B * H >= (1ll << 31) || pl.num_wg >= (1ll << 22)) return FA_ERR_SHAPE;
+  *workgroups = (int)pl.num_wg;
+  *rows_per_workgroup = pl.narrow ? fa355::Geo<128, 8, 2>::BR : fa355::Geo<128>::BR;
+  *items_per_workgroup = pl.n_rep;
+  return FA_OK;
+}
 
 }  // extern "C"
