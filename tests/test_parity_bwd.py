@@ -196,6 +196,25 @@ def test_bwd_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("dropout_p", [0.0, 0.2])
+def test_bwd_deterministic_many_workgroups(dropout_p):
+    # a grid of 16 heads x 12 key blocks per head, three calls: the weights that the dK/dV kernel's waves pass
+    # to each other through LDS, and every other exchange, must give the same bits each time
+    inp = ai.make_custom(2, 8, 1500, 1500, 128, "bf16", True, seed=90_011)
+    do = ai.make_dout((2, 8, 1500, 128), "bf16", seed=90_012).to(DEV)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd(q, k, v, causal=True, dropout_p=dropout_p, seed=77)
+    runs = []
+    for _ in range(3):
+        g = [torch.full_like(t, float("nan")) for t in (q, k, v)]
+        fa.fa_bwd(q, k, v, o, do, lse, *g, causal=True, dropout_p=dropout_p, seed=77)
+        torch.cuda.synchronize()
+        runs.append([x.cpu() for x in g])
+    for r in runs[1:]:
+        for x, y in zip(runs[0], r):
+            assert torch.equal(x, y)
+
+
 def test_flash_attention_autograd():
     inp = ai.make_custom(2, 2, 320, 320, 64, "fp16", True, seed=91_001)
     do = ai.make_dout((2, 2, 320, 64), "fp16", seed=91_002)
