@@ -813,6 +813,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           if (live) {
             u32x4 pb[KB][2];
             make_p(Sc, pb, tf, std::false_type{});
+            // (with dropout, the V reads are not hoisted over the weights: that
+            // schedule spilled a register here)
+            if constexpr (DROP) __builtin_amdgcn_sched_barrier(0);
             pv(pb, vst_rt((tf - t_b) % G::NS));
           }
           end_iter(tf);
