@@ -780,10 +780,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           constexpr int P = decltype(Pc)::value;
           using PN = std::integral_constant<int, (P + 1) % G::NS>;
           using PC = std::integral_constant<int, (P + G::NS - 1) % G::NS>;
+          using PP = std::integral_constant<int, (P + 2) % G::NS>;
           if (live) rescale(mxc);
-          if (t + G::NS - 1 < t_e) {
-            copy_k(t + G::NS - 1, PC{});
-            copy_v(t + G::NS - 1, PC{});
+          // Without dropout the waves join only after the even steps (counted from
+          // t_b).  Between two joins run an odd step t and step t+1: they read K of
+          // tiles t+1, t+2 and V of tiles t, t+1, all copied and waited for before
+          // the first join, and copy K of tiles t+3, t+4 and V of tiles t+2, t+3,
+          // whose stages (tile mod 4) are none of those read.  V of tile t+3 copied
+          // in an even step t would overwrite V of tile t-1 while a wave may still
+          // be in step t-1, so an even step leaves that copy to the next step.
+          if (t + G::NS - 1 < t_e) copy_k(t + G::NS - 1, PC{});
+          if constexpr (DROP) {
+            if (t + G::NS - 1 < t_e) copy_v(t + G::NS - 1, PC{});
+          } else if constexpr (P & 1) {
+            if (t >= t_b + 3 && t + 2 < t_e) copy_v(t + 2, PP{});
+            if (t + G::NS - 1 < t_e) copy_v(t + G::NS - 1, PC{});
+          } else {
+            if (t == t_b && t + G::NS - 1 < t_e) copy_v(t + G::NS - 1, PC{});
           }
           if (live) {
             // LLVM's interleave strategy for small-GEMM bodies (MFMAs spaced between the
@@ -796,7 +809,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             pv(pb, vst(Pc));
             mxn = row_max(Sn);
           }
-          end_iter(t);
+          if constexpr (DROP || !(P & 1)) end_iter(t);
         };
         static_assert(G::NS == 4, "the loop below is unrolled over the stages");
         for (int t = t_b; t + 1 < n_full; t += 4) {
@@ -804,6 +817,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           if (t + 2 < n_full) it_main(t + 1, sB, sA, mxB, mxA, std::integral_constant<int, 1>{});
           if (t + 3 < n_full) it_main(t + 2, sA, sB, mxA, mxB, std::integral_constant<int, 2>{});
           if (t + 4 < n_full) it_main(t + 3, sB, sA, mxB, mxA, std::integral_constant<int, 3>{});
+        }
+        // back to the copy-and-join-every-step state: after an odd last step the
+        // waves join; after an even one, V of its tile + 3 is copied
+        const int r_last = n_full - 2 - t_b;
+        if (!DROP && r_last >= 0) {
+          if (r_last & 1)
+            wait_join();
+          else if (r_last >= 2 && n_full + 1 < t_e)
+            copy_v_rt(n_full + 1);
         }
         // weights and PV of the last full tile, whose Sᵀ is already computed
         const int tf = n_full - 1;
