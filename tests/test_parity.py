@@ -163,6 +163,28 @@ def test_wide_grids(B, H, Lq, Lk, D, dtype, causal):
     compare(o, lse, O_ref, L_ref, dtype, "wide", src=inp)
 
 
+@pytest.mark.parametrize("D,dtype,causal", [(128, "bf16", False), (128, "fp16", True), (64, "bf16", False),
+                                            (64, "fp16", True)])
+def test_step_counts(D, dtype, causal):
+    # The 256-row form's software-pipelined loop joins its waves after every second step and
+    # copies tiles on a schedule that depends on the step's parity; before the last full tile
+    # and the masked tiles it returns to one join per step.  257 heads of 65 query rows (257
+    # workgroups: that form) with 1 to 10 key tiles, full or ragged, end the loop after every
+    # count of steps, odd and even, and with 0 to 3 tiles left to copy.
+    for Lk in (64, 81, 128, 145, 192, 209, 256, 273, 320, 337, 384, 401, 448, 465, 512, 529, 576, 640):
+        if causal and Lk < 65:
+            continue  # causal needs Lq <= Lk
+        seed = 32_000 + Lk + D + (1 if causal else 0)
+        inp = ai.make_custom(1, 257, 65, Lk, D, dtype, causal, seed=seed)
+        note(f"step counts H257 Lq65 Lk{Lk} D{D} {dtype} causal={causal} seed={seed}")
+        o, lse = run_gpu(inp)
+        heads = [(0, 0), (0, 128), (0, 256)]
+        sub = {x: inp[x][:, [h for _, h in heads]] for x in ("q", "k", "v")}
+        O_ref, L_ref = attention_fp64(sub["q"], sub["k"], sub["v"], inp["scale"], causal)
+        idx = [h for _, h in heads]
+        compare(o[:, idx], lse[:, idx], O_ref, L_ref, dtype, f"step counts Lk{Lk}", src={**inp, **sub})
+
+
 @pytest.mark.parametrize("D,dtype,causal", [(128, "bf16", True), (64, "fp16", False), (128, "fp16", False)])
 def test_geometry_forms(D, dtype, causal):
     # 300 heads of 520 rows (3 query tiles of 256: 900 workgroups, the 256-row form) and the first 4
