@@ -51,6 +51,27 @@ def test_dropout_forward(B, H, Lq, Lk, D, dtype, causal, p, seed):
     assert torch.equal(lse.cpu(), lse0.cpu()), "LSE must not depend on dropout"
 
 
+@pytest.mark.parametrize("D,dtype,causal,p", [(128, "bf16", True, 0.2), (64, "fp16", False, 0.6)])
+def test_dropout_forward_wide_grids(D, dtype, causal, p):
+    # The cases above run 128-row workgroups (grids of at most 256 items); 257 heads of 65
+    # rows run the 256-row form, here with 1 to 8 key tiles so that its pipelined loop, its
+    # last full tile and its masked tiles all take the dropout path.
+    for Lk in (81, 145, 256, 337, 465, 512):
+        seed = 3_000_000 + Lk + D
+        inp = ai.make_custom(1, 257, 65, Lk, D, dtype, causal, seed=140_000 + Lk + D)
+        note(f"dropout fwd wide H257 Lq65 Lk{Lk} D{D} {dtype} causal={causal} p={p} seed={seed}")
+        q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+        fa.fa_fwd_dropout(q, k, v, o, lse, causal=causal, scale=inp["scale"], dropout_p=p, seed=seed)
+        torch.cuda.synchronize()
+        heads = [(0, 0), (0, 130), (0, 256)]
+        O_ref, L_ref = attention_fp64(inp["q"], inp["k"], inp["v"], inp["scale"], causal, heads=heads,
+                                      dropout_p=p, seed=seed)
+        compare_fwd(o.cpu(), lse.cpu(), O_ref, L_ref, dtype, f"dropout fwd wide Lk{Lk}",
+                    src=dict(inp, dropout_p=p, seed=seed), heads=heads)
+
+
 @pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal,p,seed", CASES, ids=IDS)
 def test_dropout_backward(B, H, Lq, Lk, D, dtype, causal, p, seed):
     inp = ai.make_custom(B, H, Lq, Lk, D, dtype, causal, seed=120_000 + Lq + Lk)
