@@ -783,20 +783,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           using PP = std::integral_constant<int, (P + 2) % G::NS>;
           if (live) rescale(mxc);
           // Without dropout the waves join only after the even steps (counted from
-          // t_b).  Between two joins run an odd step t and step t+1: they read K of
-          // tiles t+1, t+2 and V of tiles t, t+1, all copied and waited for before
-          // the first join, and copy K of tiles t+3, t+4 and V of tiles t+2, t+3,
-          // whose stages (tile mod 4) are none of those read.  V of tile t+3 copied
-          // in an even step t would overwrite V of tile t-1 while a wave may still
-          // be in step t-1, so an even step leaves that copy to the next step.
+          // t_b), and step t copies K of tile t+3 and V of tile t+2 (V of tile t_b+2
+          // comes from the prologue).  Between two joins run an odd step t and step
+          // t+1: they read K of tiles t+1, t+2 and V of tiles t, t+1, all copied and
+          // waited for before the join that precedes them, and write K of tiles t+3,
+          // t+4 and V of tiles t+2, t+3, whose stages ((tile - t_b) mod 4) are none of
+          // those read.  With dropout every step joins and copies tile t+3.
           if (t + G::NS - 1 < t_e) copy_k(t + G::NS - 1, PC{});
           if constexpr (DROP) {
             if (t + G::NS - 1 < t_e) copy_v(t + G::NS - 1, PC{});
-          } else if constexpr (P & 1) {
-            if (t >= t_b + 3 && t + 2 < t_e) copy_v(t + 2, PP{});
-            if (t + G::NS - 1 < t_e) copy_v(t + G::NS - 1, PC{});
           } else {
-            if (t == t_b && t + G::NS - 1 < t_e) copy_v(t + G::NS - 1, PC{});
+            if (t > t_b && t + 2 < t_e) copy_v(t + 2, PP{});
           }
           if (live) {
             // LLVM's interleave strategy for small-GEMM bodies (MFMAs spaced between the
@@ -818,14 +815,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           if (t + 3 < n_full) it_main(t + 2, sA, sB, mxA, mxB, std::integral_constant<int, 2>{});
           if (t + 4 < n_full) it_main(t + 3, sB, sA, mxB, mxA, std::integral_constant<int, 3>{});
         }
-        // back to the copy-and-join-every-step state: after an odd last step the
-        // waves join; after an even one, V of its tile + 3 is copied
+        // back to the state of one join and one tile copied per step (K and V
+        // requested through tile n_full + 1): after an odd last step the waves join,
+        // then V of tile n_full + 1 is requested
         const int r_last = n_full - 2 - t_b;
         if (!DROP && r_last >= 0) {
-          if (r_last & 1)
-            wait_join();
-          else if (r_last >= 2 && n_full + 1 < t_e)
-            copy_v_rt(n_full + 1);
+          if (r_last & 1) wait_join();
+          if (n_full + 1 < t_e) copy_v_rt(n_full + 1);
         }
         // weights and PV of the last full tile, whose Sᵀ is already computed
         const int tf = n_full - 1;
